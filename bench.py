@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE gate_up hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of tokens of a routed-
+expert gate_up layer (Gemma 4 26B-A4B shapes: hidden 2048, 128 experts,
+top-8, 2 x 768 gate_up rows per expert):
+    moe_route_permute -> hadamard128_rotate -> moe_gateup_i8h_grouped (act out)
+or, for the FP8 block variant, moe_route_permute -> moe_gateup_fp8blk_grouped.
+
+Default workload: one decode token (T = 1). Inputs are seeded synthetic data
+already resident in HBM; every step takes a different token (router logits
+and activations) and a different copy of the layer's weights, so the touched
+experts stream from HBM rather than from the 256 MB last-level cache. The
+steps are captured in a HIP graph and replayed; the timed region is bracketed
+by device synchronisations.
+
+Printed: one JSON line with the step throughput (weight GB/s: bytes of the
+touched experts' codes and scales per second), tokens/s, the roofline of the
+dominant kernel (gate_up) timed with HIP events over graph replays of that
+kernel alone, and the CPU oracle timed on a bounded sample of the same steps.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+METRIC = "weight GB/s and tokens/s, MoE gate_up at M=1/128/2048; % HBM / MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", default="decode", choices=["decode", "verify", "prefill", "fp8"])
+    ap.add_argument("--copies", type=int, default=0, help="weight copies cycled (0: enough to defeat caches)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures the hot path on ONE GPU; --gpus must be 1 "
+              f"(got --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import int8_hadamard_domain_amd as i8h
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    i8h.lib()
+
+    name = args.workload
+    L = synth.layer(name)
+    fp8 = name == "fp8"
+    per_copy_bytes = L.E * L.N * L.K * (1 + (2 / (128 * 128) if fp8 else 2 / 128))
+    if args.copies > 0:
+        copies = args.copies
+    else:
+        # keep several hundred MB between reuses of any copy
+        touched = min(L.E, L.P) / L.E * per_copy_bytes
+        copies = int(min(16, max(2, np.ceil(1.6e9 / max(touched, 1)))))
+    # distinct token batches cycled by the steps
+    nb = 64 if L.T == 1 else (8 if L.T <= 128 else 4)
+    S = nb * copies // np.gcd(nb, copies)          # steps per captured graph: every (batch, copy) pair
+    while S > 256:
+        S //= 2
+    steps = max(S, (args.steps + S - 1) // S * S)
+    warm = max(S, (args.warmup + S - 1) // S * S)
+
+    t_setup = time.perf_counter()
+    LB = synth.layer(name, T=L.T * nb)
+    logits_np = synth.router_logits(LB).reshape(nb, L.T, L.E)
+    x_np = synth.activations_bf16(LB).reshape(nb, L.T, L.K)
+    if fp8:
+        codes_np, sbits_np = synth.synthetic_fp8(L)
+    else:
+        codes_np, sbits_np = synth.synthetic_i8h(L)
+    codes0 = torch.from_numpy(codes_np).to(dev)
+    scales0 = torch.from_numpy(sbits_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    codes = [codes0] + [codes0.clone() for _ in range(copies - 1)]
+    scales = [scales0] + [scales0.clone() for _ in range(copies - 1)]
+    logits = torch.from_numpy(logits_np).to(dev)
+    xs = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    k = L.topk
+    route_bufs = [dict() for _ in range(S)]
+    for b in route_bufs:
+        b["topk_ids"] = torch.empty((L.T, k), dtype=torch.int32, device=dev)
+        b["topk_w"] = torch.empty((L.T, k), dtype=torch.float32, device=dev)
+        b["expert_off"] = torch.empty((L.E + 1,), dtype=torch.int32, device=dev)
+        b["sorted_pairs"] = torch.empty((L.P,), dtype=torch.int32, device=dev)
+        b["pair_pos"] = torch.empty((L.P,), dtype=torch.int32, device=dev)
+        ws = i8h.lib().moe_route_permute_workspace_size(L.T, L.E, k)
+        b["workspace"] = torch.empty((max(ws, 1),), dtype=torch.uint8, device=dev)
+    xr = torch.empty((L.T, L.K), dtype=torch.bfloat16, device=dev)
+    act = torch.empty((L.P, L.N // 2), dtype=torch.float32, device=dev)
+    fp8_ws = torch.empty((max(i8h.lib().moe_gateup_fp8blk_workspace_size(L.T, L.K), 1),),
+                         dtype=torch.uint8, device=dev)
+
+    def gate_up(i):
+        b = route_bufs[i]
+        c = i % copies
+        if fp8:
+            i8h.moe_gateup_fp8blk_grouped(xs[i % nb], codes[c], scales[c], k, b["expert_off"], b["sorted_pairs"],
+                                          gate_up=False, act=act, workspace=fp8_ws)
+        else:
+            i8h.moe_gateup_i8h_grouped(xr, codes[c], scales[c], k, b["expert_off"], b["sorted_pairs"],
+                                       gate_up=False, act=act, path=args.path)
+
+    def step(i):
+        i8h.moe_route_permute(logits[i % nb], k, out=route_bufs[i])
+        if not fp8:
+            i8h.hadamard128_rotate(xs[i % nb], out=xr)
+        gate_up(i)
+
+    def capture(fn):
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            for i in range(S):
+                fn(i)
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize(dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(S):
+                fn(i)
+        torch.cuda.synchronize(dev)
+        return g
+
+    g_step = capture(step)
+    # touched experts of every captured step (bookkeeping only, outside the timed region)
+    touched = []
+    for i in range(S):
+        off = route_bufs[i]["expert_off"].cpu().numpy()
+        touched.append(int(np.count_nonzero(np.diff(off))))
+    setup_s = time.perf_counter() - t_setup
+
+    bytes_per_expert = L.N * L.K + (L.N // 128) * L.G * 2 if fp8 else L.N * L.K + L.N * L.G * 2
+    weight_bytes = np.array(touched, dtype=np.float64) * bytes_per_expert   # per step in the graph
+
+    for _ in range(warm // S):
+        g_step.replay()
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(steps // S):
+        g_step.replay()
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    ms_per_step = wall / steps * 1e3
+    total_weight = weight_bytes.sum() * (steps // S)
+    value = total_weight / wall / 1e9
+    tokens_per_s = L.T * steps / wall
+
+    # ---- dominant kernel: gate_up alone, HIP events around graph replays ----
+    g_gu = capture(gate_up)
+    reps = max(1, 2048 // S)
+    for _ in range(2):
+        g_gu.replay()
+    st = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    ev0.record(st)
+    for _ in range(reps):
+        g_gu.replay()
+    ev1.record(st)
+    torch.cuda.synchronize(dev)
+    kern_us = ev0.elapsed_time(ev1) * 1e3 / (reps * S)
+    # algorithmic bytes per launch: touched codes + scales, activations read once,
+    # act written, routing lists read
+    x_bytes = L.T * L.K * (1 if fp8 else 2)
+    alg_bytes = weight_bytes.mean() + x_bytes + L.P * (L.N // 2) * 4 + L.P * 4 + (L.E + 1) * 4
+    if fp8:
+        alg_bytes += L.T * L.K * 2 + L.T * L.G * 4       # quantizer reads bf16 x, writes scales
+    achieved = alg_bytes / (kern_us * 1e-6) / 1e9
+    flops = 2.0 * L.P * L.N * L.K
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "k_gateup_fp8_gemm" if fp8 else ("k_gateup_i8h_gemv" if (args.path == "gemv" or (args.path == "auto" and L.T <= 8)) else "k_gateup_i8h_gemm"),
+                "kernel_us": round(kern_us, 3), "alg_bytes_per_launch": int(alg_bytes),
+                "mfma_tflops": round(flops / (kern_us * 1e-6) / 1e12, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(L, nb, logits_np, x_np, codes_np, sbits_np, fp8, args.cpu_seconds, bytes_per_expert)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "tokens_per_s": round(tokens_per_s, 1),
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3*fp8e4m3->f32" if fp8 else "i8*bf16->f32",
+        "data": "synthetic",
+        "config": {"workload": f"{name}: T={L.T} K={L.K} E={L.E} top-{k} N={L.N} (gate_up of Gemma 4 26B-A4B)",
+                   "T": L.T, "K": L.K, "E": L.E, "topk": k, "N": L.N, "weight_copies": copies,
+                   "steps_per_graph": int(S), "touched_experts_per_step": float(np.mean(touched)),
+                   "outputs": "act (fp32); gate_up not stored", "setup_s": round(setup_s, 1)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline(L, nb, logits_np, x_np, codes_np, sbits_np, fp8, budget_s, bytes_per_expert):
+    """The fp64 oracle, as it stands, on the same steps until the budget is spent."""
+    from oracle import gateup, hadamard, numfmt, quant, router
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([d.get("num_threads", 1) for d in info] + [1])
+    except Exception:
+        cores = 1
+    scales = numfmt.bf16_from_bits(sbits_np)
+    done, wbytes, tokens = 0, 0.0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and done < nb:
+        lg = logits_np[done]
+        x = numfmt.bf16_from_bits(x_np[done])
+        r = router.route(lg, L.topk)
+        if fp8:
+            qx, sx = quant.quantize_fp8_activations(x)
+            gu = gateup.gateup_fp8blk(qx, sx, codes_np, scales, r["expert_off"], r["sorted_pairs"], L.topk)
+        else:
+            xr = hadamard.rotate_activations_bf16(x)
+            gu = gateup.gateup_i8h(xr, codes_np, scales, r["expert_off"], r["sorted_pairs"], L.topk)
+        gateup.epilogue(gu)
+        done += 1
+        wbytes += np.count_nonzero(np.diff(r["expert_off"])) * bytes_per_expert
+        tokens += L.T
+    el = time.perf_counter() - t0
+    return {"value": round(wbytes / el / 1e9, 4), "unit": "GB/s", "tokens_per_s": round(tokens / el, 3),
+            "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} step(s) of the same workload (route + rotate + gate_up + epilogue, fp64 NumPy), "
+                      f"{el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

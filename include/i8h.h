@@ -1,0 +1,183 @@
+/*
+ * i8h — routed-expert gate_up of a weight-quantized MoE layer, on one
+ * AMD Instinct MI355X (gfx950). C ABI of libi8h.so.
+ *
+ * The format comes from the model card "Gemma 4 26B-A4B-it + DFlash, int8
+ * experts — radiance container" (model table, row "Weights"; section "How
+ * this file was made", the recipe line of the routed experts' gate_up): int8
+ * codes in -127..127 stored in the 128-wide Hadamard domain, one bf16 scale
+ * per output row and per 128 of K. The FP8 variant comes from "Gemma 4
+ * 26B-A4B-it + DFlash, FP8 experts — radiance container" (model table, row
+ * "Weights"; its recipe): E4M3 codes per 128x128 block with one bf16 scale
+ * per block.
+ *
+ * Conventions shared by every call:
+ *   - All array pointers are DEVICE pointers, allocated and owned by the
+ *     caller. The library allocates nothing and keeps no state between calls.
+ *   - bf16 values travel as uint16_t bit patterns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work on it and return: no device synchronisation,
+ *     no device-to-host copy, and grid sizes never depend on device data.
+ *   - Arguments are validated on the host before anything is launched; on a
+ *     validation error nothing is enqueued. I8H_EHIP reports a launch error
+ *     from the HIP runtime. Faults during execution surface at the caller's
+ *     next synchronisation.
+ *   - T == 0 (no tokens) is a valid no-op that returns I8H_OK.
+ *   - Calls are thread-safe and reentrant; calls on different streams may
+ *     overlap as long as their output buffers do not alias.
+ *   - Row-major layouts throughout; the last index is contiguous.
+ *
+ * Sizes: T tokens, K hidden size (K % 128 == 0), E experts (1..1024),
+ * topk experts per token (1..min(E, 32)), N = 2*I gate_up rows per expert
+ * (rows 0..I-1 are the gate rows, rows I..2I-1 the matching up rows),
+ * P = T*topk (token, slot) pairs, G = K/128 groups.
+ */
+#ifndef I8H_H
+#define I8H_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  I8H_OK = 0,
+  I8H_EINVAL = -1,       /* invalid argument: null pointer, size, alignment */
+  I8H_EUNSUPPORTED = -2, /* well-formed but outside what the kernels handle */
+  I8H_EHIP = -3          /* the HIP runtime refused a launch */
+} i8h_status;
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char* i8h_status_string(int status);
+
+/* Upper limits checked by every entry point. */
+#define I8H_MAX_EXPERTS 1024
+#define I8H_MAX_TOPK 32
+
+/* ------------------------------------------------------------------------
+ * Routing: top-k over router logits, per-expert histogram, exclusive scan
+ * and a stable scatter of the (token, slot) pairs into expert-sorted order.
+ *
+ * The int8 card's model table (row "Weights") describes routed experts picked
+ * by a router; it prints no rule, so: token t takes the topk experts of
+ * largest logit, ties to the lower expert index, slot j = j-th in that order;
+ * topk_w[t, j] = softmax over the topk chosen logits (float32 arithmetic).
+ * Pair p = t*topk + j. expert_off is the exclusive scan of per-expert pair
+ * counts (expert_off[E] = P); sorted_pairs[expert_off[e] .. expert_off[e+1])
+ * lists expert e's pairs in increasing p; pair_pos[p] is the position of p
+ * in sorted_pairs. All integer outputs are deterministic, bit for bit.
+ *
+ * logits      [T, E] float32, finite (NaN or infinity: result unspecified)
+ * topk_ids    [T, topk] int32 out
+ * topk_w      [T, topk] float32 out
+ * expert_off  [E + 1] int32 out
+ * sorted_pairs[P] int32 out
+ * pair_pos    [P] int32 out
+ * workspace   device scratch of at least moe_route_permute_workspace_size()
+ *             bytes (may be NULL when that size is 0); contents on entry
+ *             are ignored. P must stay below 2^31.
+ * ---------------------------------------------------------------------- */
+size_t moe_route_permute_workspace_size(int T, int E, int topk);
+int moe_route_permute(const float* logits, int T, int E, int topk,
+                      int32_t* topk_ids, float* topk_w, int32_t* expert_off,
+                      int32_t* sorted_pairs, int32_t* pair_pos,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Blockwise 128-wide Walsh-Hadamard rotation of bf16 activation rows.
+ *
+ * The int8 card's codes live in the 128-wide Hadamard domain (model table,
+ * row "Weights"; recipe transform fwht128), so the activations must be
+ * rotated the same way before the product; the card puts this in the
+ * producer of the experts' input (row "Needs"). For every row t and block b:
+ *   y[t, 128b + i] = bf16( sum_j H[i, j] * x[t, 128b + j] / sqrt(128) ),
+ * H[i, j] = (-1)^popcount(i & j) (Sylvester, natural order). The butterflies
+ * run in float32; the result is rounded once to bf16 (nearest even).
+ *
+ * x  [T, ldx] bf16, the first K columns are read; y [T, ldy] bf16 out.
+ * ldx, ldy >= K and multiples of 8; x, y 16-byte aligned. x == y (in place)
+ * is allowed; other overlap is not.
+ * ---------------------------------------------------------------------- */
+int hadamard128_rotate(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy,
+                       int T, int K, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Grouped int8 Hadamard-domain gate_up with the fused GELU-tanh epilogue.
+ *
+ * For the pair in expert-sorted row r (expert e = the run holding r,
+ * token t = sorted_pairs[r] / topk):
+ *   gu[r, n]  = sum_g s[e, n, g] * sum_{kk in g} q[e, n, kk] * x_rot[t, kk]
+ *   act[r, i] = gelu_tanh(gu[r, i]) * gu[r, I + i],  i < I = N/2,
+ *   gelu_tanh(v) = v/2 * (1 + tanh(sqrt(2/pi) * (v + 0.044715 v^3))).
+ * The code-times-activation products are exact; sums are float32. Router
+ * weights are not applied. Output rows stay in expert-sorted order.
+ *
+ * x_rot       [T, K] bf16, already rotated (hadamard128_rotate), 16-B aligned
+ * codes       [E, N, K] int8 in -127..127, 16-B aligned
+ * scales      [E, N, K/128] bf16
+ * expert_off  [E + 1], sorted_pairs [T*topk]: as moe_route_permute writes them
+ * gate_up     [T*topk, N] float32 out, or NULL to skip storing it
+ * act         [T*topk, N/2] float32 out, or NULL to skip storing it
+ * N must be a positive multiple of 64 (gate and up halves of 32-row tiles).
+ * ---------------------------------------------------------------------- */
+int moe_gateup_i8h_grouped(const uint16_t* x_rot, int T, int K,
+                           const int8_t* codes, const uint16_t* scales,
+                           int E, int N, int topk,
+                           const int32_t* expert_off, const int32_t* sorted_pairs,
+                           float* gate_up, float* act, void* stream);
+
+/* Same as moe_gateup_i8h_grouped with the kernel chosen by the caller:
+ * I8H_PATH_AUTO (by T, as the call above), I8H_PATH_GEMV (the decode-shaped
+ * kernel: VALU dot products streaming codes with 16-byte loads) or
+ * I8H_PATH_GEMM (the verify/prefill-shaped kernel: bf16 MFMA). Both give
+ * the same result to float32 rounding. */
+enum { I8H_PATH_AUTO = 0, I8H_PATH_GEMV = 1, I8H_PATH_GEMM = 2 };
+int moe_gateup_i8h_grouped_path(const uint16_t* x_rot, int T, int K,
+                                const int8_t* codes, const uint16_t* scales,
+                                int E, int N, int topk,
+                                const int32_t* expert_off, const int32_t* sorted_pairs,
+                                float* gate_up, float* act, int path, void* stream);
+
+/* ------------------------------------------------------------------------
+ * FP8 activation quantizer: per token and per 128 of K (one float32 scale
+ * per token and 128 values, as the activations of the int8 12B card, header
+ * table row "Format"):
+ *   sx[t, g] = float32(amax_g / 448)            (IEEE single division)
+ *   qx[t, kk] = E4M3FN(x[t, kk] / sx[t, g])      (nearest even, saturating
+ *                                                at +-448; sign kept on zero)
+ * a group with sx == 0 gets qx = 0. x [T, K] bf16 (16-B aligned); qx [T, K]
+ * uint8 out (16-B aligned); sx [T, K/128] float32 out.
+ * ---------------------------------------------------------------------- */
+int fp8_quantize_activations(const uint16_t* x, int T, int K,
+                             uint8_t* qx, float* sx, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Grouped FP8 E4M3 128x128-block gate_up (FP8 card, model table row
+ * "Weights"), on gfx950's FP8 MFMA. Activations are unrotated bf16; the call
+ * first quantizes them with fp8_quantize_activations into the workspace, then
+ *   gu[r, n] = sum_g (sw[e, n/128, g] * sx[t, g])
+ *                    * sum_{kk in g} E4M3(qw[e, n, kk]) * E4M3(qx[t, kk])
+ * with the same epilogue, row order and outputs as moe_gateup_i8h_grouped.
+ *
+ * x [T, K] bf16; codes [E, N, K] E4M3FN bytes (finite); scales [E, N/128,
+ * K/128] bf16; N must be a positive multiple of 128 (whole 128-row scale
+ * blocks). Workspace layout (at least
+ * moe_gateup_fp8blk_workspace_size(T, K) bytes, 256-B aligned base): qx
+ * [T, K] uint8 at offset 0, then sx [T, K/128] float32 at offset
+ * round_up(T*K, 256). Both are left there for the caller to inspect.
+ * ---------------------------------------------------------------------- */
+size_t moe_gateup_fp8blk_workspace_size(int T, int K);
+int moe_gateup_fp8blk_grouped(const uint16_t* x, int T, int K,
+                              const uint8_t* codes, const uint16_t* scales,
+                              int E, int N, int topk,
+                              const int32_t* expert_off, const int32_t* sorted_pairs,
+                              float* gate_up, float* act,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* I8H_H */

@@ -1,0 +1,217 @@
+"""int8 Hadamard-domain MoE gate_up on AMD Instinct MI355X (gfx950).
+
+Thin Python binding over libi8h.so (C ABI declared in include/i8h.h). Every
+function here only checks tensors, allocates outputs with torch and passes
+device pointers plus torch's current HIP stream to the library; all of the
+computation runs in the library's HIP kernels. There is no CPU fallback: if
+the library is not built, or a tensor is not on the GPU, the call raises.
+
+Functions (same names as the C entry points):
+  moe_route_permute          top-k routing and the expert-sorted permutation
+  hadamard128_rotate         blockwise 128-wide Walsh-Hadamard rotation (bf16)
+  moe_gateup_i8h_grouped     grouped int8 Hadamard-domain gate_up + GELU epilogue
+  fp8_quantize_activations   per-token, per-128 E4M3 activation quantizer
+  moe_gateup_fp8blk_grouped  grouped FP8 E4M3 128x128-block gate_up + epilogue
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libi8h.so")
+
+I8H_OK, I8H_EINVAL, I8H_EUNSUPPORTED, I8H_EHIP = 0, -1, -2, -3
+PATHS = {"auto": 0, "gemv": 1, "gemm": 2}
+
+_lib = None
+
+
+class I8HError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        msg = lib().i8h_status_string(status).decode()
+        super().__init__(f"{fn} failed: {msg} ({status})")
+
+
+def lib():
+    """The loaded libi8h.so, with argument types set. Raises if not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                           "(python -m int8_hadamard_domain_amd.build_lib)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "i8h_status_string": (ctypes.c_char_p, [I]),
+        "moe_route_permute_workspace_size": (SZ, [I, I, I]),
+        "moe_route_permute": (I, [P, I, I, I, P, P, P, P, P, P, SZ, P]),
+        "hadamard128_rotate": (I, [P, I64, P, I64, I, I, P]),
+        "moe_gateup_i8h_grouped": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P]),
+        "moe_gateup_i8h_grouped_path": (I, [P, I, I, P, P, I, I, I, P, P, P, P, I, P]),
+        "fp8_quantize_activations": (I, [P, I, I, P, P, P]),
+        "moe_gateup_fp8blk_workspace_size": (SZ, [I, I]),
+        "moe_gateup_fp8blk_grouped": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P, SZ, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(fn, status):
+    if status != I8H_OK:
+        raise I8HError(fn, status)
+
+
+def _dev(t, name, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions (got {t.dim()})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def moe_route_permute(logits, topk, out=None):
+    """logits [T, E] float32 -> dict of topk_ids [T, k] int32, topk_w [T, k]
+    float32, expert_off [E+1] int32, sorted_pairs [T*k] int32, pair_pos
+    [T*k] int32 (and the workspace used). `out` may hold preallocated
+    tensors under the same keys."""
+    _dev(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    dev = logits.device
+    o = dict(out or {})
+    i32 = dict(dtype=torch.int32, device=dev)
+    o.setdefault("topk_ids", torch.empty((T, topk), **i32))
+    o.setdefault("topk_w", torch.empty((T, topk), dtype=torch.float32, device=dev))
+    o.setdefault("expert_off", torch.empty((E + 1,), **i32))
+    o.setdefault("sorted_pairs", torch.empty((T * topk,), **i32))
+    o.setdefault("pair_pos", torch.empty((T * topk,), **i32))
+    ws_bytes = lib().moe_route_permute_workspace_size(T, E, topk)
+    if "workspace" not in o or o["workspace"].numel() < ws_bytes:
+        o["workspace"] = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    _check("moe_route_permute", lib().moe_route_permute(
+        _ptr(logits), T, E, topk, _ptr(o["topk_ids"]), _ptr(o["topk_w"]), _ptr(o["expert_off"]),
+        _ptr(o["sorted_pairs"]), _ptr(o["pair_pos"]), _ptr(o["workspace"]), o["workspace"].numel(),
+        _stream(dev)))
+    return o
+
+
+def hadamard128_rotate(x, out=None):
+    """bf16 [T, K] (K % 128 == 0) -> bf16 [T, K], blockwise H x / sqrt(128).
+    `out` may be x itself (in place)."""
+    _dev(x, "x", torch.bfloat16, 2)
+    T, K = x.shape
+    y = torch.empty_like(x) if out is None else _dev(out, "out", torch.bfloat16, 2)
+    _check("hadamard128_rotate", lib().hadamard128_rotate(
+        _ptr(x), K, _ptr(y), y.shape[1], T, K, _stream(x.device)))
+    return y
+
+
+def moe_gateup_i8h_grouped(x_rot, codes, scales, topk, expert_off, sorted_pairs,
+                           gate_up=True, act=True, path="auto"):
+    """Grouped int8 Hadamard-domain gate_up.
+
+    x_rot [T, K] bf16 (rotated), codes [E, N, K] int8, scales [E, N, K/128]
+    bf16, expert_off [E+1] / sorted_pairs [T*topk] int32 from
+    moe_route_permute. gate_up / act: True to allocate, a tensor to write
+    into, or False/None to skip. Returns (gate_up, act) in expert-sorted
+    row order (None for skipped outputs).
+    """
+    _dev(x_rot, "x_rot", torch.bfloat16, 2)
+    _dev(codes, "codes", torch.int8, 3)
+    _dev(scales, "scales", torch.bfloat16, 3)
+    _dev(expert_off, "expert_off", torch.int32, 1)
+    _dev(sorted_pairs, "sorted_pairs", torch.int32, 1)
+    T, K = x_rot.shape
+    E, N, K2 = codes.shape
+    if K2 != K or scales.shape != (E, N, K // 128) or expert_off.numel() != E + 1 \
+            or sorted_pairs.numel() != T * topk:
+        raise ValueError("inconsistent shapes")
+    dev = x_rot.device
+    gu = _out(gate_up, (T * topk, N), dev)
+    ac = _out(act, (T * topk, N // 2), dev)
+    _check("moe_gateup_i8h_grouped", lib().moe_gateup_i8h_grouped_path(
+        _ptr(x_rot), T, K, _ptr(codes), _ptr(scales), E, N, topk, _ptr(expert_off), _ptr(sorted_pairs),
+        _ptr(gu), _ptr(ac), PATHS[path], _stream(dev)))
+    return gu, ac
+
+
+def _out(spec, shape, dev):
+    if spec is None or spec is False:
+        return None
+    if spec is True:
+        return torch.empty(shape, dtype=torch.float32, device=dev)
+    _dev(spec, "output", torch.float32)
+    if tuple(spec.shape) != tuple(shape):
+        raise ValueError(f"output must have shape {shape}")
+    return spec
+
+
+def fp8_quantize_activations(x, qx=None, sx=None):
+    """bf16 [T, K] -> (E4M3 codes uint8 [T, K], float32 scales [T, K/128])."""
+    _dev(x, "x", torch.bfloat16, 2)
+    T, K = x.shape
+    qx = torch.empty((T, K), dtype=torch.uint8, device=x.device) if qx is None else qx
+    sx = torch.empty((T, K // 128), dtype=torch.float32, device=x.device) if sx is None else sx
+    _check("fp8_quantize_activations", lib().fp8_quantize_activations(
+        _ptr(x), T, K, _ptr(qx), _ptr(sx), _stream(x.device)))
+    return qx, sx
+
+
+def moe_gateup_fp8blk_grouped(x, codes, scales, topk, expert_off, sorted_pairs,
+                              gate_up=True, act=True, workspace=None):
+    """Grouped FP8 E4M3 128x128-block gate_up.
+
+    x [T, K] bf16 (not rotated), codes [E, N, K] uint8 (E4M3 bytes), scales
+    [E, N/128, K/128] bf16. Returns (gate_up, act, workspace); the workspace
+    holds the quantized activations (qx [T, K] uint8 at offset 0, then sx
+    [T, K/128] float32 at the next multiple of 256 bytes).
+    """
+    _dev(x, "x", torch.bfloat16, 2)
+    _dev(codes, "codes", torch.uint8, 3)
+    _dev(scales, "scales", torch.bfloat16, 3)
+    _dev(expert_off, "expert_off", torch.int32, 1)
+    _dev(sorted_pairs, "sorted_pairs", torch.int32, 1)
+    T, K = x.shape
+    E, N, K2 = codes.shape
+    if K2 != K or scales.shape != (E, N // 128, K // 128) or expert_off.numel() != E + 1 \
+            or sorted_pairs.numel() != T * topk:
+        raise ValueError("inconsistent shapes")
+    dev = x.device
+    need = lib().moe_gateup_fp8blk_workspace_size(T, K)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    gu = _out(gate_up, (T * topk, N), dev)
+    ac = _out(act, (T * topk, N // 2), dev)
+    _check("moe_gateup_fp8blk_grouped", lib().moe_gateup_fp8blk_grouped(
+        _ptr(x), T, K, _ptr(codes), _ptr(scales), E, N, topk, _ptr(expert_off), _ptr(sorted_pairs),
+        _ptr(gu), _ptr(ac), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return gu, ac, workspace
+
+
+def fp8_workspace_views(workspace, T, K):
+    """(qx [T, K] uint8, sx [T, K/128] float32) views of a gate_up workspace."""
+    off = (T * K + 255) // 256 * 256
+    qx = workspace[:T * K].view(T, K)
+    sx = workspace[off:off + T * (K // 128) * 4].view(torch.float32).view(T, K // 128)
+    return qx, sx

@@ -1,0 +1,160 @@
+// C ABI of libi8h: host-side validation, kernel choice and launch.
+// Every check runs before any HIP call, so an invalid call has no effect.
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/i8h.h"
+#include "launch.hpp"
+
+namespace {
+
+using i8h::kMaxExperts;
+using i8h::kMaxTopk;
+
+constexpr int kGemvMaxK = 4096;   // the decode kernel keeps K/1024 pieces per lane
+constexpr int kGemvMaxT = 8;      // AUTO picks the decode kernel up to this many tokens
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline int from_hip(hipError_t e) { return e == hipSuccess ? I8H_OK : I8H_EHIP; }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int check_common_moe(int T, int K, int E, int N, int topk) {
+  if (T < 0 || K <= 0 || (K % 128) != 0 || E <= 0 || N <= 0 || topk <= 0) return I8H_EINVAL;
+  if (E > kMaxExperts || topk > kMaxTopk || topk > E) return I8H_EUNSUPPORTED;
+  if ((int64_t)T * topk >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;
+  return I8H_OK;
+}
+
+int gateup_i8h(const uint16_t* x_rot, int T, int K, const int8_t* codes, const uint16_t* scales, int E, int N,
+               int topk, const int32_t* expert_off, const int32_t* sorted_pairs, float* gate_up, float* act,
+               int path, void* stream) {
+  int rc = check_common_moe(T, K, E, N, topk);
+  if (rc != I8H_OK) return rc;
+  if ((N % 64) != 0) return I8H_EINVAL;
+  if (path != I8H_PATH_AUTO && path != I8H_PATH_GEMV && path != I8H_PATH_GEMM) return I8H_EINVAL;
+  if (T == 0) return I8H_OK;
+  if (!x_rot || !codes || !scales || !expert_off || !sorted_pairs) return I8H_EINVAL;
+  if (!aligned(x_rot, 16) || !aligned(codes, 16) || !aligned(scales, 2)) return I8H_EINVAL;
+  if (!aligned(expert_off, 4) || !aligned(sorted_pairs, 4)) return I8H_EINVAL;
+  if ((gate_up && !aligned(gate_up, 4)) || (act && !aligned(act, 4))) return I8H_EINVAL;
+  if (!gate_up && !act) return I8H_OK;  // nothing requested
+  if (path == I8H_PATH_GEMV && K > kGemvMaxK) return I8H_EUNSUPPORTED;
+  if (path == I8H_PATH_AUTO) path = (T <= kGemvMaxT && K <= kGemvMaxK) ? I8H_PATH_GEMV : I8H_PATH_GEMM;
+  hipError_t e;
+  if (path == I8H_PATH_GEMV)
+    e = i8h::launch_gateup_i8h_gemv(x_rot, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up,
+                                    act, as_stream(stream));
+  else
+    e = i8h::launch_gateup_i8h_gemm(x_rot, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up,
+                                    act, as_stream(stream));
+  return from_hip(e);
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+const char* i8h_status_string(int status) {
+  switch (status) {
+    case I8H_OK: return "ok";
+    case I8H_EINVAL: return "invalid argument";
+    case I8H_EUNSUPPORTED: return "unsupported size";
+    case I8H_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_route_permute_workspace_size(int T, int E, int topk) {
+  if (T <= 0 || E <= 0 || topk <= 0 || E > kMaxExperts || topk > kMaxTopk) return 0;
+  return i8h::route_workspace_bytes(T, E, topk);
+}
+
+int moe_route_permute(const float* logits, int T, int E, int topk, int32_t* topk_ids, float* topk_w,
+                      int32_t* expert_off, int32_t* sorted_pairs, int32_t* pair_pos, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (T < 0 || E <= 0 || topk <= 0) return I8H_EINVAL;
+  if (E > kMaxExperts || topk > kMaxTopk || topk > E) return I8H_EUNSUPPORTED;
+  if ((int64_t)T * topk >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;
+  if (T == 0) return I8H_OK;
+  if (!logits || !topk_ids || !topk_w || !expert_off || !sorted_pairs || !pair_pos) return I8H_EINVAL;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(expert_off, 4) ||
+      !aligned(sorted_pairs, 4) || !aligned(pair_pos, 4))
+    return I8H_EINVAL;
+  size_t need = i8h::route_workspace_bytes(T, E, topk);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 4))) return I8H_EINVAL;
+  return from_hip(i8h::launch_route(logits, T, E, topk, topk_ids, topk_w, expert_off, sorted_pairs, pair_pos,
+                                    workspace, as_stream(stream)));
+}
+
+int hadamard128_rotate(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy, int T, int K, void* stream) {
+  if (T < 0 || K <= 0 || (K % 128) != 0) return I8H_EINVAL;
+  if (ldx < K || ldy < K || (ldx % 8) != 0 || (ldy % 8) != 0) return I8H_EINVAL;
+  if (T == 0) return I8H_OK;
+  if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return I8H_EINVAL;
+  if (x != y) {
+    // other overlap would let one block read what another already wrote
+    uintptr_t xb = reinterpret_cast<uintptr_t>(x), yb = reinterpret_cast<uintptr_t>(y);
+    uintptr_t xe = xb + 2 * (uintptr_t)((int64_t)(T - 1) * ldx + K);
+    uintptr_t ye = yb + 2 * (uintptr_t)((int64_t)(T - 1) * ldy + K);
+    if (xb < ye && yb < xe) return I8H_EINVAL;
+  } else if (ldx != ldy) {
+    return I8H_EINVAL;
+  }
+  return from_hip(i8h::launch_fwht128(x, ldx, y, ldy, T, K, as_stream(stream)));
+}
+
+int moe_gateup_i8h_grouped(const uint16_t* x_rot, int T, int K, const int8_t* codes, const uint16_t* scales, int E,
+                           int N, int topk, const int32_t* expert_off, const int32_t* sorted_pairs,
+                           float* gate_up, float* act, void* stream) {
+  return gateup_i8h(x_rot, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up, act,
+                    I8H_PATH_AUTO, stream);
+}
+
+int moe_gateup_i8h_grouped_path(const uint16_t* x_rot, int T, int K, const int8_t* codes, const uint16_t* scales,
+                                int E, int N, int topk, const int32_t* expert_off, const int32_t* sorted_pairs,
+                                float* gate_up, float* act, int path, void* stream) {
+  return gateup_i8h(x_rot, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up, act, path,
+                    stream);
+}
+
+int fp8_quantize_activations(const uint16_t* x, int T, int K, uint8_t* qx, float* sx, void* stream) {
+  if (T < 0 || K <= 0 || (K % 128) != 0) return I8H_EINVAL;
+  if (T == 0) return I8H_OK;
+  if (!x || !qx || !sx || !aligned(x, 16) || !aligned(qx, 16) || !aligned(sx, 4)) return I8H_EINVAL;
+  return from_hip(i8h::launch_fp8_act_quant(x, T, K, qx, sx, as_stream(stream)));
+}
+
+size_t moe_gateup_fp8blk_workspace_size(int T, int K) {
+  if (T <= 0 || K <= 0 || (K % 128) != 0) return 0;
+  return round_up((size_t)T * K, 256) + round_up((size_t)T * (K / 128) * sizeof(float), 256);
+}
+
+int moe_gateup_fp8blk_grouped(const uint16_t* x, int T, int K, const uint8_t* codes, const uint16_t* scales, int E,
+                              int N, int topk, const int32_t* expert_off, const int32_t* sorted_pairs,
+                              float* gate_up, float* act, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  int rc = check_common_moe(T, K, E, N, topk);
+  if (rc != I8H_OK) return rc;
+  if ((N % 128) != 0) return I8H_EINVAL;
+  if (T == 0) return I8H_OK;
+  if (!x || !codes || !scales || !expert_off || !sorted_pairs) return I8H_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(expert_off, 4) ||
+      !aligned(sorted_pairs, 4))
+    return I8H_EINVAL;
+  if ((gate_up && !aligned(gate_up, 4)) || (act && !aligned(act, 4))) return I8H_EINVAL;
+  size_t need = moe_gateup_fp8blk_workspace_size(T, K);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return I8H_EINVAL;
+  if (!gate_up && !act) return I8H_OK;
+  uint8_t* qx = static_cast<uint8_t*>(workspace);
+  float* sx = reinterpret_cast<float*>(qx + round_up((size_t)T * K, 256));
+  hipError_t e = i8h::launch_fp8_act_quant(x, T, K, qx, sx, as_stream(stream));
+  if (e != hipSuccess) return I8H_EHIP;
+  return from_hip(i8h::launch_gateup_fp8(qx, sx, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs,
+                                         gate_up, act, as_stream(stream)));
+}
+
+}  // extern "C"

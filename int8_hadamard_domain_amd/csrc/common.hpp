@@ -1,0 +1,59 @@
+// Shared device helpers for the gfx950 kernels of libi8h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace i8h {
+
+constexpr int kWave = 64;      // CDNA wavefront width
+constexpr int kGroup = 128;    // K per scale group and per Hadamard block
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 bits -> float (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Signed byte j of a dword -> float (exact; v_cvt_f32_i32 with a sign-extended
+// byte select).
+template <int J>
+__device__ __forceinline__ float sbyte(uint32_t w) {
+  return (float)(int8_t)((w >> (8 * J)) & 0xffu);
+}
+
+// Wave-wide float sum with a fixed reduction tree (deterministic).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// GELU, tanh approximation: v/2 (1 + tanh(z)) with z = sqrt(2/pi)(v + 0.044715 v^3).
+// Evaluated as v / (1 + exp(-2z)), the same function written without the
+// cancellation of 1 + tanh(z) for negative z.
+__device__ __forceinline__ float gelu_tanh(float v) {
+  const float c = 0.7978845608028654f;  // sqrt(2/pi)
+  float z = c * (v + 0.044715f * v * v * v);
+  return v / (1.0f + expf(-2.0f * z));
+}
+
+__host__ __device__ constexpr inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace i8h

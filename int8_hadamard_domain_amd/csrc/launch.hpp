@@ -1,0 +1,33 @@
+// Internal launchers, called by the C ABI after host-side validation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace i8h {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopk = 32;
+
+size_t route_workspace_bytes(int T, int E, int k);
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                        int32_t* expert_off, int32_t* sorted_pairs, int32_t* pair_pos,
+                        void* ws, hipStream_t st);
+
+hipError_t launch_fwht128(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy, int T, int K,
+                          hipStream_t st);
+
+hipError_t launch_gateup_i8h_gemv(const uint16_t* xrot, int T, int K, const int8_t* codes,
+                                  const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
+                                  const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st);
+hipError_t launch_gateup_i8h_gemm(const uint16_t* xrot, int T, int K, const int8_t* codes,
+                                  const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
+                                  const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st);
+
+hipError_t launch_fp8_act_quant(const uint16_t* x, int T, int K, uint8_t* qx, float* sx, hipStream_t st);
+hipError_t launch_gateup_fp8(const uint8_t* qx, const float* sx, int T, int K, const uint8_t* codes,
+                             const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
+                             const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st);
+
+}  // namespace i8h

@@ -1,0 +1,270 @@
+// Router permutation: top-k over logits, per-expert histogram, exclusive scan
+// and a stable scatter of (token, slot) pairs into expert-sorted order.
+//
+// Rule (the int8 card's model table, row "Weights", describes routed experts
+// picked by a router and prints no rule): token t takes the k experts of
+// largest logit, ties to the lower expert index; the weights are the softmax
+// over the k chosen logits. Pairs p = t*k + j are grouped by expert with
+// increasing p inside each expert (stable), which makes every integer
+// output unique and lets the GPU reproduce it bit for bit: ranks come from
+// ballots in lane order and fixed block order, never from atomic arrival order.
+//
+// Kernels
+//   k_route_topk     one wave per token (grid T/4 x 256 threads)
+//   k_route_count    per chunk of 256 pairs: histogram over experts (LDS)
+//   k_route_scatter  per chunk: totals + exclusive scan + in-chunk stable ranks
+//   k_route_small    T <= 4: the three steps in one block (decode shape)
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace i8h {
+
+constexpr int kChunkPairs = 256;   // pairs per histogram/scatter block
+constexpr int kRouteThreads = 256;
+
+// --- top-k of one token, by one wave ------------------------------------
+// Lane l holds logits e = l + 64 v. Each round takes the wave-wide best
+// (largest value, then lowest index), then retires it.
+template <int VPL>
+__device__ __forceinline__ void topk_one_token(const float* __restrict__ row, int E, int k, int lane,
+                                               int32_t* __restrict__ ids_out, float* __restrict__ w_out,
+                                               int* lds_ids /* may be null */) {
+  float v[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    int e = lane + kWave * i;
+    v[i] = e < E ? row[e] : 0.0f;
+  }
+  uint32_t retired = 0;  // bit i: v[i] already taken
+  int my_id = 0;
+  float my_logit = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    // best of this lane: indices grow with i, so a strict '>' keeps the lowest tie
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      int e = lane + kWave * i;
+      bool open = e < E && !((retired >> i) & 1u);
+      if (open && (bi == 0x7fffffff || v[i] > bv)) { bv = v[i]; bi = e; }
+    }
+    // wave-wide best: larger value first, then lower index (a total order,
+    // so every lane ends with the same winner)
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      float ov = __shfl_xor(bv, m, kWave);
+      int oi = __shfl_xor(bi, m, kWave);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    if ((bi % kWave) == lane) retired |= 1u << (bi / kWave);
+    if (lane == j) { my_id = bi; my_logit = bv; }
+  }
+  float l0 = __shfl(my_logit, 0, kWave);
+  float ex = lane < k ? expf(my_logit - l0) : 0.0f;
+  float sum = wave_sum(ex);
+  if (lane < k) {
+    ids_out[lane] = my_id;
+    w_out[lane] = ex / sum;
+    if (lds_ids) lds_ids[lane] = my_id;
+  }
+}
+
+template <int VPL>
+__global__ void __launch_bounds__(kRouteThreads)
+k_route_topk(const float* __restrict__ logits, int T, int E, int k,
+             int32_t* __restrict__ ids, float* __restrict__ w) {
+  int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  int t = blockIdx.x * (kRouteThreads / kWave) + wave;
+  if (t >= T) return;
+  topk_one_token<VPL>(logits + (size_t)t * E, E, k, lane, ids + (size_t)t * k, w + (size_t)t * k, nullptr);
+}
+
+// --- histogram of one chunk of pairs -------------------------------------
+__global__ void __launch_bounds__(kRouteThreads)
+k_route_count(const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ hist) {
+  __shared__ int cnt[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  int p = blockIdx.x * kChunkPairs + threadIdx.x;
+  if (p < P) atomicAdd(&cnt[ids[p]], 1);   // counts only: order does not matter
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// Exclusive scan of tot[0..E) in LDS into off[0..E), block of 256 threads,
+// each owning 4 consecutive experts. Returns nothing; off[E] is not written.
+__device__ __forceinline__ void block_exclusive_scan(const int* tot, int* off, int E, int* wave_tot) {
+  int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  int base = tid * 4;
+  int a[4];
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = (base + i < E) ? tot[base + i] : 0;
+    s += a[i];
+  }
+  // inclusive wave scan of per-thread sums
+  int inc = s;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int o = __shfl_up(inc, d, kWave);
+    if (lane >= d) inc += o;
+  }
+  if (lane == kWave - 1) wave_tot[wave] = inc;
+  __syncthreads();
+  int wofs = 0;
+  for (int w = 0; w < wave; ++w) wofs += wave_tot[w];
+  int run = wofs + inc - s;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (base + i < E) off[base + i] = run;
+    run += a[i];
+  }
+}
+
+// Stable in-block ranks: thread tid holds pair p (valid) with expert e.
+// Returns the rank of p among the block's pairs of the same expert with a
+// lower thread index. wcount is [4][E] in LDS, zero on entry, zero on exit.
+__device__ __forceinline__ int block_stable_rank(bool valid, int e, int E, int nbits, int* wcount) {
+  int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  uint64_t mask = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    bool bit = valid && ((e >> b) & 1);
+    uint64_t bal = __ballot(bit);
+    mask &= bit ? bal : ~bal;
+  }
+  uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int rank_w = __popcll(mask & lower);
+  int cnt_w = __popcll(mask);
+  if (valid && rank_w == 0) wcount[wave * E + e] = cnt_w;
+  __syncthreads();
+  int prefix = 0;
+  if (valid)
+    for (int w = 0; w < wave; ++w) prefix += wcount[w * E + e];
+  __syncthreads();
+  if (valid && rank_w == 0) wcount[wave * E + e] = 0;
+  return prefix + rank_w;
+}
+
+__device__ __forceinline__ int bits_for(int E) {
+  int nb = 0;
+  while ((1 << nb) < E) ++nb;
+  return nb;
+}
+
+// --- totals, scan and stable scatter of one chunk ------------------------
+__global__ void __launch_bounds__(kRouteThreads)
+k_route_scatter(const int32_t* __restrict__ ids, int P, int E, int nchunks,
+                const int32_t* __restrict__ hist, int32_t* __restrict__ expert_off,
+                int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos) {
+  __shared__ int tot[kMaxExperts];
+  __shared__ int base[kMaxExperts];
+  __shared__ int pre[kMaxExperts];
+  __shared__ int wcount[4 * kMaxExperts];
+  __shared__ int wave_tot[4];
+  int c = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int t = 0, before = 0;
+    for (int cc = 0; cc < nchunks; ++cc) {
+      int h = hist[(size_t)cc * E + e];
+      t += h;
+      if (cc < c) before += h;
+    }
+    tot[e] = t;
+    pre[e] = before;
+  }
+  for (int i = threadIdx.x; i < 4 * E; i += blockDim.x) wcount[i] = 0;
+  __syncthreads();
+  block_exclusive_scan(tot, base, E, wave_tot);
+  __syncthreads();
+  if (c == 0) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) expert_off[e] = base[e];
+    if (threadIdx.x == 0) expert_off[E] = P;
+  }
+  int p = c * kChunkPairs + threadIdx.x;
+  bool valid = p < P;
+  int e = valid ? ids[p] : 0;
+  int rank = block_stable_rank(valid, e, E, bits_for(E), wcount);
+  if (valid) {
+    int dst = base[e] + pre[e] + rank;
+    sorted_pairs[dst] = p;
+    pair_pos[p] = dst;
+  }
+}
+
+// --- T <= 4: everything in one block --------------------------------------
+template <int VPL>
+__global__ void __launch_bounds__(kRouteThreads)
+k_route_small(const float* __restrict__ logits, int T, int E, int k,
+              int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ expert_off,
+              int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos) {
+  __shared__ int lds_ids[4 * kMaxTopk];
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int base[kMaxExperts];
+  __shared__ int wcount[4 * kMaxExperts];
+  __shared__ int wave_tot[4];
+  int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  for (int i = threadIdx.x; i < 4 * E; i += blockDim.x) wcount[i] = 0;
+  if (wave < T)
+    topk_one_token<VPL>(logits + (size_t)wave * E, E, k, lane, ids + (size_t)wave * k, w + (size_t)wave * k,
+                        lds_ids + wave * k);
+  __syncthreads();
+  int P = T * k;
+  int p = threadIdx.x;
+  bool valid = p < P;
+  int e = valid ? lds_ids[p] : 0;
+  if (valid) atomicAdd(&cnt[e], 1);
+  __syncthreads();
+  block_exclusive_scan(cnt, base, E, wave_tot);
+  __syncthreads();
+  for (int i = threadIdx.x; i < E; i += blockDim.x) expert_off[i] = base[i];
+  if (threadIdx.x == 0) expert_off[E] = P;
+  int rank = block_stable_rank(valid, e, E, bits_for(E), wcount);
+  if (valid) {
+    int dst = base[e] + rank;
+    sorted_pairs[dst] = p;
+    pair_pos[p] = dst;
+  }
+}
+
+size_t route_workspace_bytes(int T, int E, int k) {
+  if (T <= 4) return 0;
+  size_t P = (size_t)T * k;
+  size_t nchunks = (P + kChunkPairs - 1) / kChunkPairs;
+  return nchunks * (size_t)E * sizeof(int32_t);
+}
+
+#define I8H_TOPK_DISPATCH(KERNEL, ...)                                   \
+  do {                                                                   \
+    if (vpl <= 1) KERNEL<1><<<grid, kRouteThreads, 0, st>>>(__VA_ARGS__);  \
+    else if (vpl <= 2) KERNEL<2><<<grid, kRouteThreads, 0, st>>>(__VA_ARGS__); \
+    else if (vpl <= 4) KERNEL<4><<<grid, kRouteThreads, 0, st>>>(__VA_ARGS__); \
+    else if (vpl <= 8) KERNEL<8><<<grid, kRouteThreads, 0, st>>>(__VA_ARGS__); \
+    else KERNEL<16><<<grid, kRouteThreads, 0, st>>>(__VA_ARGS__);        \
+  } while (0)
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                        int32_t* expert_off, int32_t* sorted_pairs, int32_t* pair_pos,
+                        void* ws, hipStream_t st) {
+  int vpl = cdiv(E, kWave);
+  if (T <= 4) {
+    dim3 grid(1);
+    I8H_TOPK_DISPATCH(k_route_small, logits, T, E, k, ids, w, expert_off, sorted_pairs, pair_pos);
+    return hipGetLastError();
+  }
+  {
+    dim3 grid(cdiv(T, kRouteThreads / kWave));
+    I8H_TOPK_DISPATCH(k_route_topk, logits, T, E, k, ids, w);
+  }
+  int P = T * k;
+  int nchunks = cdiv(P, kChunkPairs);
+  int32_t* hist = static_cast<int32_t*>(ws);
+  k_route_count<<<nchunks, kRouteThreads, 0, st>>>(ids, P, E, hist);
+  k_route_scatter<<<nchunks, kRouteThreads, 0, st>>>(ids, P, E, nchunks, hist, expert_off, sorted_pairs,
+                                                     pair_pos);
+  return hipGetLastError();
+}
+
+}  // namespace i8h

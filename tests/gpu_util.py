@@ -1,0 +1,87 @@
+"""Helpers shared by the GPU parity tests: tolerance checks, bf16 near-tie
+analysis for the rotation, and device upload of generator data.
+
+Tolerance for float32 outputs (gate_up and act) against the fp64 oracle:
+elementwise |gpu - oracle| <= 1e-4 |oracle| + 1e-5.
+"""
+
+import numpy as np
+import torch
+
+from oracle import hadamard, numfmt
+
+RTOL, ATOL = 1e-4, 1e-5
+
+
+def assert_close(gpu, ref, what, rtol=RTOL, atol=ATOL):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU values"
+    err = np.abs(gpu - ref)
+    lim = rtol * np.abs(ref) + atol
+    bad = err > lim
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside |d| <= {rtol}|ref| + {atol}; "
+                             f"worst ratio {np.max(err / lim):.3g}; first {idx.tolist()} "
+                             f"gpu={gpu[tuple(idx[0])]!r} ref={ref[tuple(idx[0])]!r}")
+
+
+def cuda(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype) if t.dtype.itemsize == dtype.itemsize and t.dtype != dtype else t.to(dtype)
+    return t.cuda()
+
+
+def bf16_cuda(bits):
+    """uint16 bf16 bit patterns (numpy) -> bf16 tensor on the GPU."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def bf16_bits_of(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def fwht_tie_window(x):
+    """Per-output bound on how far the float32 rotation (7 butterfly stages,
+    one multiply by a rounded 1/sqrt(128)) can sit from the exact value:
+    (7 + 2) * 2^-24 * sum_j |x_j| / sqrt(128), per 128-block, with margin."""
+    xb = np.abs(np.asarray(x, dtype=np.float64)).reshape(x.shape[0], -1, 128)
+    s = xb.sum(-1, keepdims=True) / np.sqrt(128.0)
+    return np.broadcast_to(12 * 2.0 ** -24 * s, xb.shape).reshape(x.shape)
+
+
+def near_tie_mask(exact, window):
+    """True where the exact value lies within `window` of the midpoint
+    between its two neighbouring bf16 values (where a float32 evaluation
+    may round either way)."""
+    ae = np.abs(np.asarray(exact, dtype=np.float64))
+    ar = numfmt.bf16_round(ae)
+    bits = numfmt.bf16_to_bits(ar).astype(np.int64)
+    other_bits = np.where(ae >= ar, bits + 1, np.maximum(bits - 1, 0))
+    other = numfmt.bf16_from_bits(other_bits.astype(np.uint16))
+    mid = (ar + other) / 2
+    return np.abs(ae - mid) <= window
+
+
+def check_rotation(x_bits, y_bits):
+    """GPU rotation y (bf16 bits) of x (bf16 bits) against the oracle: equal
+    everywhere except at proven near-ties, where the two results must be
+    adjacent bf16 values. Returns the number of near-tie differences."""
+    x = numfmt.bf16_from_bits(x_bits)
+    exact = hadamard.rotate_blocks(x)
+    want = numfmt.bf16_round(exact)
+    got = numfmt.bf16_from_bits(y_bits)
+    diff = got != want
+    if not diff.any():
+        return 0
+    win = fwht_tie_window(x)
+    tie = near_tie_mask(exact, win)
+    assert np.all(tie[diff]), f"{(diff & ~tie).sum()} differences away from any rounding tie"
+    gb = numfmt.bf16_to_bits(got[diff]).astype(np.int64)
+    wb = numfmt.bf16_to_bits(want[diff]).astype(np.int64)
+    # adjacent bf16 values: bit patterns differ by one (same sign), or +-0 vs smallest
+    assert np.all(np.abs(gb - wb) == 1), "a near-tie difference larger than one bf16 step"
+    return int(diff.sum())

@@ -1,0 +1,123 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/i8h.h declares, and rejects invalid arguments on the host
+with the documented status codes before anything is launched. The invalid
+calls pass dummy non-null addresses that are never dereferenced."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import int8_hadamard_domain_amd as i8h
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "i8h.h")
+
+EINVAL, EUNSUP, OK = i8h.I8H_EINVAL, i8h.I8H_EUNSUPPORTED, i8h.I8H_OK
+A = ctypes.c_void_p(0x10000)     # a 256-byte aligned dummy address, never touched
+ODD = ctypes.c_void_p(0x10002)   # misaligned for 4/16-byte data
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z][a-z0-9_]*)\s*\(", src)) - {"defined"})
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(i8h.LIB_PATH):
+        pytest.skip("libi8h.so not built")
+    return i8h.lib()
+
+
+def test_every_declared_function_is_exported(L):
+    names = declared_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    assert L.i8h_status_string(0) == b"ok"
+    assert L.i8h_status_string(-1) == b"invalid argument"
+    assert L.i8h_status_string(-2) == b"unsupported size"
+    assert L.i8h_status_string(-3) == b"HIP launch error"
+    assert L.i8h_status_string(7) == b"unknown status"
+
+
+def test_workspace_sizes(L):
+    assert L.moe_route_permute_workspace_size(1, 128, 8) == 0          # single-block path
+    assert L.moe_route_permute_workspace_size(2048, 128, 8) == 64 * 128 * 4
+    assert L.moe_route_permute_workspace_size(0, 128, 8) == 0
+    assert L.moe_gateup_fp8blk_workspace_size(128, 2048) == 128 * 2048 + 128 * 16 * 4
+    assert L.moe_gateup_fp8blk_workspace_size(3, 128) == 512 + 256    # each part rounded to 256 B
+
+
+def route(L, T=8, E=16, k=2, ptr=A, ws=A, wsb=1 << 20):
+    return L.moe_route_permute(ptr, T, E, k, A, A, A, A, A, ws, wsb, None)
+
+
+def test_route_validation(L):
+    assert route(L, T=-1) == EINVAL
+    assert route(L, E=0) == EINVAL
+    assert route(L, k=0) == EINVAL
+    assert route(L, E=1025) == EUNSUP
+    assert route(L, E=64, k=33) == EUNSUP
+    assert route(L, E=4, k=5) == EUNSUP
+    assert route(L, T=0) == OK                       # no-op
+    assert route(L, ptr=None) == EINVAL
+    assert route(L, ptr=ODD) == EINVAL
+    assert route(L, T=100, ws=None) == EINVAL        # workspace needed
+    assert route(L, T=100, wsb=16) == EINVAL         # too small
+    assert route(L, T=1 << 27, k=16, E=64) == EUNSUP  # P overflows int32
+
+
+def rot(L, x=A, ldx=256, y=A, ldy=256, T=4, K=256):
+    return L.hadamard128_rotate(x, ldx, y, ldy, T, K, None)
+
+
+def test_rotate_validation(L):
+    assert rot(L, K=200) == EINVAL
+    assert rot(L, K=0) == EINVAL
+    assert rot(L, ldx=128) == EINVAL                 # ldx < K
+    assert rot(L, ldy=260) == EINVAL                 # not a multiple of 8
+    assert rot(L, x=None) == EINVAL
+    assert rot(L, x=ctypes.c_void_p(0x10008)) == EINVAL
+    assert rot(L, T=0) == OK
+    # partial overlap of distinct x and y
+    assert rot(L, x=ctypes.c_void_p(0x10000), y=ctypes.c_void_p(0x10100)) == EINVAL
+    # in place with different strides
+    assert rot(L, ldy=264) == EINVAL
+
+
+def gemm(L, x=A, T=4, K=256, codes=A, scales=A, E=8, N=256, k=2, off=A, sp=A, gu=A, act=A, path=0):
+    return L.moe_gateup_i8h_grouped_path(x, T, K, codes, scales, E, N, k, off, sp, gu, act, path, None)
+
+
+def test_gateup_i8h_validation(L):
+    assert gemm(L, K=100) == EINVAL
+    assert gemm(L, N=96) == EINVAL                   # N % 64
+    assert gemm(L, E=2000) == EUNSUP
+    assert gemm(L, k=3, E=2) == EUNSUP
+    assert gemm(L, path=7) == EINVAL
+    assert gemm(L, T=0) == OK
+    assert gemm(L, x=None) == EINVAL
+    assert gemm(L, codes=ODD) == EINVAL
+    assert gemm(L, gu=ODD) == EINVAL
+    assert gemm(L, gu=None, act=None) == OK          # nothing requested
+    assert gemm(L, K=8192, path=1) == EUNSUP         # decode kernel keeps K <= 4096
+    assert L.moe_gateup_i8h_grouped(None, 4, 256, A, A, 8, 256, 2, A, A, A, A, None) == EINVAL
+
+
+def test_fp8_validation(L):
+    f = L.moe_gateup_fp8blk_grouped
+    assert f(A, 4, 256, A, A, 8, 192, 2, A, A, A, A, A, 1 << 20, None) == EINVAL    # N % 128
+    assert f(A, 4, 256, A, A, 8, 256, 2, A, A, A, A, None, 1 << 20, None) == EINVAL  # no workspace
+    assert f(A, 4, 256, A, A, 8, 256, 2, A, A, A, A, A, 16, None) == EINVAL         # too small
+    assert f(A, 4, 256, A, A, 8, 256, 2, A, A, A, A, ctypes.c_void_p(0x10010), 1 << 20, None) == EINVAL
+    assert f(A, 0, 256, A, A, 8, 256, 2, A, A, A, A, None, 0, None) == OK
+    q = L.fp8_quantize_activations
+    assert q(A, 4, 100, A, A, None) == EINVAL
+    assert q(ODD, 4, 128, A, A, None) == EINVAL
+    assert q(A, 0, 128, A, A, None) == OK

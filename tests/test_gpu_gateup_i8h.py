@@ -1,0 +1,239 @@
+"""GPU parity: moe_gateup_i8h_grouped (both kernels) against the oracle.
+
+Elementwise |gpu - oracle| <= 1e-4 |oracle| + 1e-5 on gate_up and act. The
+product kernels are fed the oracle's rotated activations and routing, so
+each comparison checks one step. Small layers go through the oracle's own
+quantizer; the full-size layers (decode, verify, prefill) use codes drawn by
+the generator and are checked on sampled expert-sorted rows, covering every
+column of each. An end-to-end test chains route -> rotate -> gate_up on the
+GPU and widens the tolerance only by the proven near-tie bound of the bf16
+rotation.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import int8_hadamard_domain_amd as i8h
+import synth
+from oracle import gateup, hadamard, numfmt, quant, router
+from tests.gpu_util import assert_close, bf16_bits_of, bf16_cuda, fwht_tie_window, near_tie_mask
+
+pytestmark = pytest.mark.gpu
+
+PATHS = ("gemv", "gemm")
+
+
+def quantized_layer(L):
+    """Dense weights -> rotation -> int8 codes via the oracle quantizer."""
+    w = np.stack([synth.dense_weights(L, e) for e in range(L.E)]).astype(np.float64)
+    codes, scales, _ = quant.quantize_i8h(hadamard.rotate_blocks(w))
+    return codes, numfmt.bf16_to_bits(scales)
+
+
+def run_gpu(x_rot_bits, codes, scale_bits, off, sp, k, path, want_gu=True, want_act=True):
+    return i8h.moe_gateup_i8h_grouped(
+        bf16_cuda(x_rot_bits), torch.from_numpy(codes).cuda(), bf16_cuda(scale_bits), k,
+        torch.from_numpy(off.astype(np.int32)).cuda(), torch.from_numpy(sp.astype(np.int32)).cuda(),
+        gate_up=want_gu, act=want_act, path=path)
+
+
+def compare(gu, act, x_rot, codes, scale_bits, off, sp, k, rows=None, what=""):
+    torch.cuda.synchronize()
+    scales = numfmt.bf16_from_bits(scale_bits)
+    ref = gateup.gateup_i8h(x_rot, codes, scales, off, sp, k, rows=rows)
+    sel = slice(None) if rows is None else np.asarray(rows)
+    if gu is not None:
+        assert_close(gu.cpu().numpy()[sel], ref, what + " gate_up")
+    if act is not None:
+        assert_close(act.cpu().numpy()[sel], gateup.epilogue(ref), what + " act")
+
+
+def oracle_inputs(L, T=None):
+    lg = synth.router_logits(L)
+    x = synth.bf16_bits_to_f64(synth.activations_bf16(L))
+    x_rot = hadamard.rotate_activations_bf16(x)
+    r = router.route(lg, L.topk)
+    return x_rot, numfmt.bf16_to_bits(x_rot), r
+
+
+def sample_rows(off, n_extra, seed):
+    """First and last row of every non-empty expert, plus random rows."""
+    off = np.asarray(off)
+    rows = set()
+    for e in range(off.size - 1):
+        if off[e + 1] > off[e]:
+            rows.add(int(off[e]))
+            rows.add(int(off[e + 1] - 1))
+    rng = np.random.default_rng(seed)
+    rows.update(rng.integers(0, off[-1], n_extra).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    L = synth.layer("tiny")
+    codes, sbits = quantized_layer(L)
+    x_rot, xrb, r = oracle_inputs(L)
+    return L, codes, sbits, x_rot, xrb, r
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_tiny_layer(gpu_available, tiny, path):
+    L, codes, sbits, x_rot, xrb, r = tiny
+    print(f"gateup tiny {path}", flush=True)
+    gu, act = run_gpu(xrb, codes, sbits, r["expert_off"], r["sorted_pairs"], L.topk, path)
+    compare(gu, act, x_rot, codes, sbits, r["expert_off"], r["sorted_pairs"], L.topk, what=f"tiny/{path}")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_mid_layer_oracle_quantized(gpu_available, path):
+    # real K and N, several m-tiles per expert, ragged expert loads
+    L = synth.layer("verify", T=40, E=8, topk=3)
+    codes, sbits = quantized_layer(L)
+    x_rot, xrb, r = oracle_inputs(L)
+    print(f"gateup mid {path}", flush=True)
+    gu, act = run_gpu(xrb, codes, sbits, r["expert_off"], r["sorted_pairs"], L.topk, path)
+    compare(gu, act, x_rot, codes, sbits, r["expert_off"], r["sorted_pairs"], L.topk, what=f"mid/{path}")
+
+
+_FULL = {}
+
+
+def full_layer(name):
+    if name not in _FULL:
+        L = synth.layer(name)
+        codes, sbits = synth.synthetic_i8h(L)
+        x_rot, xrb, r = oracle_inputs(L)
+        dev = dict(codes=torch.from_numpy(codes).cuda(), scales=bf16_cuda(sbits), x=bf16_cuda(xrb),
+                   off=torch.from_numpy(r["expert_off"]).cuda(), sp=torch.from_numpy(r["sorted_pairs"]).cuda())
+        _FULL.clear()   # keep one full layer resident at a time
+        _FULL[name] = (L, codes, sbits, x_rot, r, dev)
+    return _FULL[name]
+
+
+@pytest.mark.parametrize("name", ["decode", "verify", "prefill"])
+@pytest.mark.parametrize("path", ("auto",) + PATHS)
+def test_full_size_sampled(gpu_available, name, path):
+    L, codes, sbits, x_rot, r, d = full_layer(name)
+    print(f"gateup full {name} {path}", flush=True)
+    gu, act = i8h.moe_gateup_i8h_grouped(d["x"], d["codes"], d["scales"], L.topk, d["off"], d["sp"], path=path)
+    rows = sample_rows(r["expert_off"], 48, seed=L.seed)
+    compare(gu, act, x_rot, codes, sbits, r["expert_off"], r["sorted_pairs"], L.topk, rows=rows,
+            what=f"{name}/{path}")
+
+
+def _random_case(T, K, E, k, N, seed, code_range=127, xscale=1.0, scale_mag=4e-4):
+    rng = np.random.default_rng(seed)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    r = router.route(lg, k)
+    xb = synth.to_bf16_bits((rng.standard_normal((T, K)) * xscale).astype(np.float32))
+    codes = rng.integers(-code_range, code_range + 1, size=(E, N, K)).astype(np.int8)
+    sb = synth.to_bf16_bits((rng.uniform(0.5, 2.0, (E, N, K // 128)) * scale_mag).astype(np.float32))
+    return numfmt.bf16_from_bits(xb), xb, codes, sb, r
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("T,K,E,k,N", [
+    (300, 256, 1, 1, 64),      # one expert, five m-passes, the smallest N
+    (5, 128, 64, 2, 128),      # one group, many empty experts
+    (7, 4096, 4, 4, 192),      # k == E, the decode kernel's largest K
+    (33, 384, 3, 2, 320),      # ragged everything
+    (1, 2048, 128, 8, 1536),   # one decode token
+])
+def test_edge_shapes(gpu_available, path, T, K, E, k, N):
+    x, xb, codes, sb, r = _random_case(T, K, E, k, N, seed=T + K + E + k + N)
+    print(f"gateup edge {path} T={T} K={K} E={E} k={k} N={N}", flush=True)
+    gu, act = run_gpu(xb, codes, sb, r["expert_off"], r["sorted_pairs"], k, path)
+    compare(gu, act, x, codes, sb, r["expert_off"], r["sorted_pairs"], k, what=f"edge/{path}")
+
+
+def test_gemm_only_large_k(gpu_available):
+    x, xb, codes, sb, r = _random_case(6, 8192, 3, 2, 128, seed=11)
+    gu, act = run_gpu(xb, codes, sb, r["expert_off"], r["sorted_pairs"], 2, "auto")
+    compare(gu, act, x, codes, sb, r["expert_off"], r["sorted_pairs"], 2, what="K8192")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_extreme_values(gpu_available, path):
+    # full-range codes, large activations, scales spanning many octaves, a zero scale
+    rng = np.random.default_rng(12)
+    T, K, E, k, N = 9, 512, 4, 2, 128
+    x, xb, codes, sb, r = _random_case(T, K, E, k, N, seed=12, xscale=300.0)
+    codes[:, :, :64] = 127
+    codes[:, 3, :] = -127
+    s = numfmt.bf16_from_bits(sb)
+    s *= np.exp2(rng.integers(-20, 20, s.shape))
+    s[0, 5, 1] = 0.0
+    sb = numfmt.bf16_to_bits(numfmt.bf16_round(s))
+    gu, act = run_gpu(xb, codes, sb, r["expert_off"], r["sorted_pairs"], k, path)
+    compare(gu, act, x, codes, sb, r["expert_off"], r["sorted_pairs"], k, what=f"extreme/{path}")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_single_output(gpu_available, tiny, path):
+    L, codes, sbits, x_rot, xrb, r = tiny
+    gu, act = run_gpu(xrb, codes, sbits, r["expert_off"], r["sorted_pairs"], L.topk, path, want_gu=False)
+    assert gu is None
+    compare(None, act, x_rot, codes, sbits, r["expert_off"], r["sorted_pairs"], L.topk, what="act only")
+    gu, act = run_gpu(xrb, codes, sbits, r["expert_off"], r["sorted_pairs"], L.topk, path, want_act=False)
+    compare(gu, None, x_rot, codes, sbits, r["expert_off"], r["sorted_pairs"], L.topk, what="gu only")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_deterministic(gpu_available, path):
+    L, codes, sbits, x_rot, r, d = full_layer("verify")
+    a = i8h.moe_gateup_i8h_grouped(d["x"], d["codes"], d["scales"], L.topk, d["off"], d["sp"], path=path)
+    b = i8h.moe_gateup_i8h_grouped(d["x"], d["codes"], d["scales"], L.topk, d["off"], d["sp"], path=path)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_end_to_end_on_gpu(gpu_available, name):
+    """route -> rotate -> gate_up, all on the GPU, against the oracle chain."""
+    L = synth.layer(name)
+    if name == "tiny":
+        codes, sbits = quantized_layer(L)
+    else:
+        lg0 = synth.router_logits(L)
+        used = sorted(set(router.topk(lg0, L.topk)[0].reshape(-1).tolist()))
+        c_used, s_used = synth.synthetic_i8h(L, experts=used)
+        codes = np.zeros((L.E, L.N, L.K), dtype=np.int8)
+        sbits = np.zeros((L.E, L.N, L.G), dtype=np.uint16)
+        codes[used], sbits[used] = c_used, s_used
+    lg = synth.router_logits(L)
+    xb = synth.activations_bf16(L)
+    x = synth.bf16_bits_to_f64(xb)
+    # oracle chain
+    r = router.route(lg, L.topk)
+    exact = hadamard.rotate_blocks(x)
+    x_rot = numfmt.bf16_round(exact)
+    scales = numfmt.bf16_from_bits(sbits)
+    ref = gateup.gateup_i8h(x_rot, codes, scales, r["expert_off"], r["sorted_pairs"], L.topk)
+    # GPU chain
+    ro = i8h.moe_route_permute(torch.from_numpy(lg).cuda(), L.topk)
+    xr = i8h.hadamard128_rotate(bf16_cuda(xb))
+    gu, act = i8h.moe_gateup_i8h_grouped(xr, torch.from_numpy(codes).cuda(), bf16_cuda(sbits), L.topk,
+                                         ro["expert_off"], ro["sorted_pairs"])
+    torch.cuda.synchronize()
+    assert np.array_equal(ro["sorted_pairs"].cpu().numpy(), r["sorted_pairs"])
+    # where the rotation may round either way, allow one bf16 step of x_rot
+    tie = near_tie_mask(exact, fwht_tie_window(x))
+    ulp = np.ldexp(1.0, np.frexp(np.abs(x_rot) + 1e-300)[1] - 8)
+    slack_x = np.where(tie, ulp, 0.0)                         # [T, K]
+    off, sp = r["expert_off"], r["sorted_pairs"]
+    what = quant.dequantize_i8h(codes, scales)
+    slack = np.zeros_like(ref)
+    for row in range(ref.shape[0]):
+        e = np.searchsorted(off, row, side="right") - 1
+        slack[row] = np.abs(what[e]) @ slack_x[sp[row] // L.topk]
+    g = gu.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(g - ref) <= 1e-4 * np.abs(ref) + 1e-5 + slack)
+    # act: bound the effect of the gate/up slack through gelu (|gelu'| < 1.13)
+    I = L.N // 2
+    ref_act = gateup.epilogue(ref)
+    dg, du = slack[:, :I], slack[:, I:]
+    act_slack = 1.13 * dg * (np.abs(ref[:, I:]) + du) + np.abs(gateup.gelu_tanh(ref[:, :I])) * du
+    a = act.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(a - ref_act) <= 1e-4 * np.abs(ref_act) + 1e-5 + act_slack)
