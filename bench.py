@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
+    ap.add_argument("--unfused", action="store_true",
+                    help="rotate with hadamard128_rotate, then moe_gateup_i8h_grouped (default for decode: "
+                         "moe_gateup_i8h_grouped_fused, rotation inside the gate_up kernel)")
     return ap.parse_args()
 
 
@@ -70,6 +73,7 @@ def main():
     name = args.workload
     L = synth.layer(name)
     fp8 = name == "fp8"
+    fused = (not fp8) and (not args.unfused) and args.path == "auto" and L.T <= 8
     per_copy_bytes = L.E * L.N * L.K * (1 + (2 / (128 * 128) if fp8 else 2 / 128))
     if args.copies > 0:
         copies = args.copies
@@ -121,13 +125,16 @@ def main():
         if fp8:
             i8h.moe_gateup_fp8blk_grouped(xs[i % nb], codes[c], scales[c], k, b["expert_off"], b["sorted_pairs"],
                                           gate_up=False, act=act, workspace=fp8_ws)
+        elif fused:
+            i8h.moe_gateup_i8h_grouped_fused(xs[i % nb], codes[c], scales[c], k, b["expert_off"],
+                                             b["sorted_pairs"], gate_up=False, act=act)
         else:
             i8h.moe_gateup_i8h_grouped(xr, codes[c], scales[c], k, b["expert_off"], b["sorted_pairs"],
                                        gate_up=False, act=act, path=args.path)
 
     def step(i):
         i8h.moe_route_permute(logits[i % nb], k, out=route_bufs[i])
-        if not fp8:
+        if not fp8 and not fused:
             i8h.hadamard128_rotate(xs[i % nb], out=xr)
         gate_up(i)
 
@@ -193,9 +200,15 @@ def main():
         alg_bytes += L.T * L.K * 2 + L.T * L.G * 4       # quantizer reads bf16 x, writes scales
     achieved = alg_bytes / (kern_us * 1e-6) / 1e9
     flops = 2.0 * L.P * L.N * L.K
+    if fp8:
+        kernel_name = "k_gateup_gemm<E4M3> (+ k_fp8_act_quant)"
+    elif args.path == "gemv" or (args.path == "auto" and L.T <= 8):
+        kernel_name = "k_gateup_i8h_gemv" + ("<rotation fused>" if fused else "")
+    else:
+        kernel_name = "k_gateup_gemm<I8>"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "k_gateup_fp8_gemm" if fp8 else ("k_gateup_i8h_gemv" if (args.path == "gemv" or (args.path == "auto" and L.T <= 8)) else "k_gateup_i8h_gemm"),
+                "kernel": kernel_name,
                 "kernel_us": round(kern_us, 3), "alg_bytes_per_launch": int(alg_bytes),
                 "mfma_tflops": round(flops / (kern_us * 1e-6) / 1e12, 2)}
 
@@ -209,8 +222,8 @@ def main():
         "unit": "GB/s",
         "tokens_per_s": round(tokens_per_s, 1),
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": warm,
+        "steps": int(steps),
+        "warmup": int(warm),
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -218,9 +231,12 @@ def main():
         "dtype": "fp8e4m3*fp8e4m3->f32" if fp8 else "i8*bf16->f32",
         "data": "synthetic",
         "config": {"workload": f"{name}: T={L.T} K={L.K} E={L.E} top-{k} N={L.N} (gate_up of Gemma 4 26B-A4B)",
-                   "T": L.T, "K": L.K, "E": L.E, "topk": k, "N": L.N, "weight_copies": copies,
+                   "T": L.T, "K": L.K, "E": L.E, "topk": k, "N": L.N, "weight_copies": int(copies),
                    "steps_per_graph": int(S), "touched_experts_per_step": float(np.mean(touched)),
-                   "outputs": "act (fp32); gate_up not stored", "setup_s": round(setup_s, 1)},
+                   "outputs": "act (fp32); gate_up not stored", "setup_s": round(setup_s, 1),
+                   "step": ("route -> gate_up (FP8 quantizer + product)" if fp8 else
+                            "route -> gate_up with the rotation fused" if fused else
+                            "route -> rotate -> gate_up")},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -116,7 +116,7 @@ int hadamard128_rotate(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy,
  *
  * x_rot       [T, K] bf16, already rotated (hadamard128_rotate), 16-B aligned
  * codes       [E, N, K] int8 in -127..127, 16-B aligned
- * scales      [E, N, K/128] bf16
+ * scales      [E, N, K/128] bf16, 4-byte aligned
  * expert_off  [E + 1], sorted_pairs [T*topk]: as moe_route_permute writes them
  * gate_up     [T*topk, N] float32 out, or NULL to skip storing it
  * act         [T*topk, N/2] float32 out, or NULL to skip storing it
@@ -140,6 +140,25 @@ int moe_gateup_i8h_grouped_path(const uint16_t* x_rot, int T, int K,
                                 const int32_t* expert_off, const int32_t* sorted_pairs,
                                 float* gate_up, float* act, int path, void* stream);
 
+/* Same product with the rotation fused in: x is the UNROTATED bf16
+ * activation [T, K]. The 128-wide Walsh-Hadamard rotation of
+ * hadamard128_rotate is applied on the fly (the int8 card's model table, row
+ * "Needs", puts the rotation in the producer of the experts' input; this call
+ * is that fusion for callers whose producer does not rotate). For few tokens
+ * (T <= 8, K <= 4096) the decode-shaped kernel rotates in its prologue and
+ * the workspace is unused; otherwise the call rotates into the workspace and
+ * runs the MFMA kernel. workspace: at least
+ * moe_gateup_i8h_fused_workspace_size(T, K) bytes, 256-B aligned (may be NULL
+ * when that size is 0). Results equal moe_gateup_i8h_grouped on the rotated
+ * activations up to float32 rounding order in the rotation. */
+size_t moe_gateup_i8h_fused_workspace_size(int T, int K);
+int moe_gateup_i8h_grouped_fused(const uint16_t* x, int T, int K,
+                                 const int8_t* codes, const uint16_t* scales,
+                                 int E, int N, int topk,
+                                 const int32_t* expert_off, const int32_t* sorted_pairs,
+                                 float* gate_up, float* act,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * FP8 activation quantizer: per token and per 128 of K (one float32 scale
  * per token and 128 values, as the activations of the int8 12B card, header
@@ -155,18 +174,21 @@ int fp8_quantize_activations(const uint16_t* x, int T, int K,
 
 /* ------------------------------------------------------------------------
  * Grouped FP8 E4M3 128x128-block gate_up (FP8 card, model table row
- * "Weights"), on gfx950's FP8 MFMA. Activations are unrotated bf16; the call
- * first quantizes them with fp8_quantize_activations into the workspace, then
+ * "Weights"). Activations are unrotated bf16; the call first quantizes them
+ * as fp8_quantize_activations does, into the workspace, then
  *   gu[r, n] = sum_g (sw[e, n/128, g] * sx[t, g])
  *                    * sum_{kk in g} E4M3(qw[e, n, kk]) * E4M3(qx[t, kk])
  * with the same epilogue, row order and outputs as moe_gateup_i8h_grouped.
  *
  * x [T, K] bf16; codes [E, N, K] E4M3FN bytes (finite); scales [E, N/128,
  * K/128] bf16; N must be a positive multiple of 128 (whole 128-row scale
- * blocks). Workspace layout (at least
+ * blocks). The products of decoded codes are exact and summed in float32
+ * (the codes are expanded to bf16 for bf16 MFMA; gfx950's FP8 MFMA keeps
+ * only about 13 bits below its largest product). Workspace (at least
  * moe_gateup_fp8blk_workspace_size(T, K) bytes, 256-B aligned base): qx
- * [T, K] uint8 at offset 0, then sx [T, K/128] float32 at offset
- * round_up(T*K, 256). Both are left there for the caller to inspect.
+ * [T, K] uint8 at offset 0, sx [T, K/128] float32 at offset
+ * A = round_up(T*K, 256), the exact bf16 values of qx [T, K] at offset
+ * A + round_up(4*T*(K/128), 256). All are left there for the caller.
  * ---------------------------------------------------------------------- */
 size_t moe_gateup_fp8blk_workspace_size(int T, int K);
 int moe_gateup_fp8blk_grouped(const uint16_t* x, int T, int K,

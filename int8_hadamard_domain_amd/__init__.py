@@ -10,6 +10,7 @@ Functions (same names as the C entry points):
   moe_route_permute          top-k routing and the expert-sorted permutation
   hadamard128_rotate         blockwise 128-wide Walsh-Hadamard rotation (bf16)
   moe_gateup_i8h_grouped     grouped int8 Hadamard-domain gate_up + GELU epilogue
+  moe_gateup_i8h_grouped_fused  the same on unrotated activations (rotation fused)
   fp8_quantize_activations   per-token, per-128 E4M3 activation quantizer
   moe_gateup_fp8blk_grouped  grouped FP8 E4M3 128x128-block gate_up + epilogue
 """
@@ -52,6 +53,8 @@ def lib():
         "hadamard128_rotate": (I, [P, I64, P, I64, I, I, P]),
         "moe_gateup_i8h_grouped": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P]),
         "moe_gateup_i8h_grouped_path": (I, [P, I, I, P, P, I, I, I, P, P, P, P, I, P]),
+        "moe_gateup_i8h_fused_workspace_size": (SZ, [I, I]),
+        "moe_gateup_i8h_grouped_fused": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P, SZ, P]),
         "fp8_quantize_activations": (I, [P, I, I, P, P, P]),
         "moe_gateup_fp8blk_workspace_size": (SZ, [I, I]),
         "moe_gateup_fp8blk_grouped": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P, SZ, P]),
@@ -156,6 +159,34 @@ def moe_gateup_i8h_grouped(x_rot, codes, scales, topk, expert_off, sorted_pairs,
     return gu, ac
 
 
+def moe_gateup_i8h_grouped_fused(x, codes, scales, topk, expert_off, sorted_pairs,
+                                 gate_up=True, act=True, workspace=None):
+    """moe_gateup_i8h_grouped on UNROTATED bf16 activations x [T, K]: the
+    128-wide Hadamard rotation is applied inside the call. Returns
+    (gate_up, act)."""
+    _dev(x, "x", torch.bfloat16, 2)
+    _dev(codes, "codes", torch.int8, 3)
+    _dev(scales, "scales", torch.bfloat16, 3)
+    _dev(expert_off, "expert_off", torch.int32, 1)
+    _dev(sorted_pairs, "sorted_pairs", torch.int32, 1)
+    T, K = x.shape
+    E, N, K2 = codes.shape
+    if K2 != K or scales.shape != (E, N, K // 128) or expert_off.numel() != E + 1 \
+            or sorted_pairs.numel() != T * topk:
+        raise ValueError("inconsistent shapes")
+    dev = x.device
+    need = lib().moe_gateup_i8h_fused_workspace_size(T, K)
+    if need > 0 and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    gu = _out(gate_up, (T * topk, N), dev)
+    ac = _out(act, (T * topk, N // 2), dev)
+    _check("moe_gateup_i8h_grouped_fused", lib().moe_gateup_i8h_grouped_fused(
+        _ptr(x), T, K, _ptr(codes), _ptr(scales), E, N, topk, _ptr(expert_off), _ptr(sorted_pairs),
+        _ptr(gu), _ptr(ac), _ptr(workspace) if need > 0 else None, 0 if workspace is None else workspace.numel(),
+        _stream(dev)))
+    return gu, ac
+
+
 def _out(spec, shape, dev):
     if spec is None or spec is False:
         return None
@@ -184,8 +215,7 @@ def moe_gateup_fp8blk_grouped(x, codes, scales, topk, expert_off, sorted_pairs,
 
     x [T, K] bf16 (not rotated), codes [E, N, K] uint8 (E4M3 bytes), scales
     [E, N/128, K/128] bf16. Returns (gate_up, act, workspace); the workspace
-    holds the quantized activations (qx [T, K] uint8 at offset 0, then sx
-    [T, K/128] float32 at the next multiple of 256 bytes).
+    holds the quantized activations (see fp8_workspace_views).
     """
     _dev(x, "x", torch.bfloat16, 2)
     _dev(codes, "codes", torch.uint8, 3)
@@ -210,8 +240,13 @@ def moe_gateup_fp8blk_grouped(x, codes, scales, topk, expert_off, sorted_pairs,
 
 
 def fp8_workspace_views(workspace, T, K):
-    """(qx [T, K] uint8, sx [T, K/128] float32) views of a gate_up workspace."""
-    off = (T * K + 255) // 256 * 256
+    """(qx [T, K] uint8, sx [T, K/128] float32, xq [T, K] bf16) views of a
+    moe_gateup_fp8blk_grouped workspace: codes, scales and the codes' exact
+    bf16 values."""
+    up = lambda v: (v + 255) // 256 * 256
+    a = up(T * K)
+    b = a + up(T * (K // 128) * 4)
     qx = workspace[:T * K].view(T, K)
-    sx = workspace[off:off + T * (K // 128) * 4].view(torch.float32).view(T, K // 128)
-    return qx, sx
+    sx = workspace[a:a + T * (K // 128) * 4].view(torch.float32).view(T, K // 128)
+    xq = workspace[b:b + T * K * 2].view(torch.bfloat16).view(T, K)
+    return qx, sx, xq

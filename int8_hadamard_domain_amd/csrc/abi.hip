@@ -24,8 +24,11 @@ int check_common_moe(int T, int K, int E, int N, int topk) {
   if (T < 0 || K <= 0 || (K % 128) != 0 || E <= 0 || N <= 0 || topk <= 0) return I8H_EINVAL;
   if (E > kMaxExperts || topk > kMaxTopk || topk > E) return I8H_EUNSUPPORTED;
   if ((int64_t)T * topk >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;
+  if ((int64_t)T * K >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;  // activation offsets are 32-bit
   return I8H_OK;
 }
+
+inline bool auto_gemv(int T, int K) { return T <= kGemvMaxT && K <= kGemvMaxK; }
 
 int gateup_i8h(const uint16_t* x_rot, int T, int K, const int8_t* codes, const uint16_t* scales, int E, int N,
                int topk, const int32_t* expert_off, const int32_t* sorted_pairs, float* gate_up, float* act,
@@ -36,12 +39,12 @@ int gateup_i8h(const uint16_t* x_rot, int T, int K, const int8_t* codes, const u
   if (path != I8H_PATH_AUTO && path != I8H_PATH_GEMV && path != I8H_PATH_GEMM) return I8H_EINVAL;
   if (T == 0) return I8H_OK;
   if (!x_rot || !codes || !scales || !expert_off || !sorted_pairs) return I8H_EINVAL;
-  if (!aligned(x_rot, 16) || !aligned(codes, 16) || !aligned(scales, 2)) return I8H_EINVAL;
+  if (!aligned(x_rot, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return I8H_EINVAL;
   if (!aligned(expert_off, 4) || !aligned(sorted_pairs, 4)) return I8H_EINVAL;
   if ((gate_up && !aligned(gate_up, 4)) || (act && !aligned(act, 4))) return I8H_EINVAL;
   if (!gate_up && !act) return I8H_OK;  // nothing requested
   if (path == I8H_PATH_GEMV && K > kGemvMaxK) return I8H_EUNSUPPORTED;
-  if (path == I8H_PATH_AUTO) path = (T <= kGemvMaxT && K <= kGemvMaxK) ? I8H_PATH_GEMV : I8H_PATH_GEMM;
+  if (path == I8H_PATH_AUTO) path = auto_gemv(T, K) ? I8H_PATH_GEMV : I8H_PATH_GEMM;
   hipError_t e;
   if (path == I8H_PATH_GEMV)
     e = i8h::launch_gateup_i8h_gemv(x_rot, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up,
@@ -53,6 +56,16 @@ int gateup_i8h(const uint16_t* x_rot, int T, int K, const int8_t* codes, const u
 }
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// FP8 workspace: qx [T, K] uint8, sx [T, K/128] float32, xq [T, K] bf16
+struct Fp8Ws {
+  size_t sx_off, xq_off, total;
+  Fp8Ws(int T, int K) {
+    sx_off = round_up((size_t)T * K, 256);
+    xq_off = sx_off + round_up((size_t)T * (K / 128) * sizeof(float), 256);
+    total = xq_off + round_up((size_t)T * K * 2, 256);
+  }
+};
 
 }  // namespace
 
@@ -125,12 +138,42 @@ int fp8_quantize_activations(const uint16_t* x, int T, int K, uint8_t* qx, float
   if (T < 0 || K <= 0 || (K % 128) != 0) return I8H_EINVAL;
   if (T == 0) return I8H_OK;
   if (!x || !qx || !sx || !aligned(x, 16) || !aligned(qx, 16) || !aligned(sx, 4)) return I8H_EINVAL;
-  return from_hip(i8h::launch_fp8_act_quant(x, T, K, qx, sx, as_stream(stream)));
+  return from_hip(i8h::launch_fp8_act_quant(x, T, K, qx, sx, nullptr, as_stream(stream)));
 }
 
 size_t moe_gateup_fp8blk_workspace_size(int T, int K) {
   if (T <= 0 || K <= 0 || (K % 128) != 0) return 0;
-  return round_up((size_t)T * K, 256) + round_up((size_t)T * (K / 128) * sizeof(float), 256);
+  return Fp8Ws(T, K).total;
+}
+
+size_t moe_gateup_i8h_fused_workspace_size(int T, int K) {
+  if (T <= 0 || K <= 0 || (K % 128) != 0) return 0;
+  return auto_gemv(T, K) ? 0 : round_up((size_t)T * K * 2, 256);
+}
+
+int moe_gateup_i8h_grouped_fused(const uint16_t* x, int T, int K, const int8_t* codes, const uint16_t* scales, int E,
+                                 int N, int topk, const int32_t* expert_off, const int32_t* sorted_pairs,
+                                 float* gate_up, float* act, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  int rc = check_common_moe(T, K, E, N, topk);
+  if (rc != I8H_OK) return rc;
+  if ((N % 64) != 0) return I8H_EINVAL;
+  if (T == 0) return I8H_OK;
+  if (!x || !codes || !scales || !expert_off || !sorted_pairs) return I8H_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return I8H_EINVAL;
+  if (!aligned(expert_off, 4) || !aligned(sorted_pairs, 4)) return I8H_EINVAL;
+  if ((gate_up && !aligned(gate_up, 4)) || (act && !aligned(act, 4))) return I8H_EINVAL;
+  size_t need = moe_gateup_i8h_fused_workspace_size(T, K);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return I8H_EINVAL;
+  if (!gate_up && !act) return I8H_OK;
+  hipStream_t st = as_stream(stream);
+  if (auto_gemv(T, K))
+    return from_hip(i8h::launch_gateup_i8h_gemv_rot(x, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs,
+                                                    gate_up, act, st));
+  uint16_t* xr = static_cast<uint16_t*>(workspace);
+  if (i8h::launch_fwht128(x, K, xr, K, T, K, st) != hipSuccess) return I8H_EHIP;
+  return from_hip(i8h::launch_gateup_i8h_gemm(xr, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs,
+                                               gate_up, act, st));
 }
 
 int moe_gateup_fp8blk_grouped(const uint16_t* x, int T, int K, const uint8_t* codes, const uint16_t* scales, int E,
@@ -142,18 +185,20 @@ int moe_gateup_fp8blk_grouped(const uint16_t* x, int T, int K, const uint8_t* co
   if ((N % 128) != 0) return I8H_EINVAL;
   if (T == 0) return I8H_OK;
   if (!x || !codes || !scales || !expert_off || !sorted_pairs) return I8H_EINVAL;
-  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(expert_off, 4) ||
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(expert_off, 4) ||
       !aligned(sorted_pairs, 4))
     return I8H_EINVAL;
   if ((gate_up && !aligned(gate_up, 4)) || (act && !aligned(act, 4))) return I8H_EINVAL;
   size_t need = moe_gateup_fp8blk_workspace_size(T, K);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return I8H_EINVAL;
   if (!gate_up && !act) return I8H_OK;
+  Fp8Ws lay(T, K);
   uint8_t* qx = static_cast<uint8_t*>(workspace);
-  float* sx = reinterpret_cast<float*>(qx + round_up((size_t)T * K, 256));
-  hipError_t e = i8h::launch_fp8_act_quant(x, T, K, qx, sx, as_stream(stream));
+  float* sx = reinterpret_cast<float*>(qx + lay.sx_off);
+  uint16_t* xq = reinterpret_cast<uint16_t*>(qx + lay.xq_off);
+  hipError_t e = i8h::launch_fp8_act_quant(x, T, K, qx, sx, xq, as_stream(stream));
   if (e != hipSuccess) return I8H_EHIP;
-  return from_hip(i8h::launch_gateup_fp8(qx, sx, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs,
+  return from_hip(i8h::launch_gateup_fp8(xq, sx, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs,
                                          gate_up, act, as_stream(stream)));
 }
 

@@ -1,0 +1,355 @@
+// Verify/prefill-shaped grouped gate_up on bf16 MFMA, for both weight formats.
+//
+// int8 Hadamard-domain (int8 card, model table row "Weights"): int8 codes in
+// -127..127, one bf16 scale per row and 128 of K; activations rotated bf16.
+//   gu[r, n] = sum_g s[e, n, g] * sum_{kk in g} q[e, n, kk] * x_rot[t, kk]
+// FP8 E4M3 128x128 blocks (FP8 card, model table row "Weights"): one bf16
+// scale per block; activations quantized per token and 128 of K (float32
+// scale sx, E4M3 codes qx, handed over here as their exact bf16 values).
+//   gu[r, n] = sum_g (sw[e, n/128, g] * sx[t, g]) * sum_{kk in g} qw * qx
+// Both: act[r, i] = gelu_tanh(gu[r, i]) * gu[r, I + i].
+//
+// Work unit = (expert e, 128 gate rows + the 128 matching up rows). Blocks
+// are mapped so that the units of one expert run on one XCD (the hardware
+// hands consecutive workgroups to the 8 XCDs in turn) and share its L2 for
+// the expert's activation rows. A unit walks the expert's pairs in passes of
+// 128 rows, so each code byte leaves HBM once per pass. Eight waves (two per
+// SIMD: one wave's MFMAs overlap the other's converts and folds) split the
+// unit: wave w owns gate rows i0..i0+31 and up rows I+i0..I+i0+31 with
+// i0 = 32 (w % 4), for pass rows 64 (w / 4) .. +63 (two m-tiles), so the gate
+// and up values of an output meet in one lane.
+//
+// Pipeline: K is cut into stages of 64 (half a scale group). Everything a
+// stage needs travels global -> LDS on gfx950's DMA path (global_load_lds: no
+// registers held while in flight) into a ring of 4 LDS slots, three stages
+// ahead of the one being multiplied: both operands as 16-byte pieces
+// XOR-swizzled by row so that fragment reads hit distinct banks, and, with
+// the second stage of each group, the group's scales (int8) or block scales
+// and per-row activation factors (E4M3) as aligned dwords. The copies are
+// issued from inline assembly: the loop then holds no memory operation the
+// compiler tracks, and each stage waits for exactly its own copies
+// (s_waitcnt vmcnt(8): the copies of the two stages issued after it may stay
+// in flight) before a workgroup barrier. v_mfma_f32_32x32x16_bf16
+// accumulates a whole 128-K group into a temporary tile that is then folded
+// into the float32 result with the group's scale (main += tmp * s); scaling
+// the codes first would round each weight to bf16. Codes become bf16
+// exactly: int8 by sign-extended byte converts (|q| <= 127 fits bf16's 8
+// significand bits), E4M3 by v_cvt_pk_f32_fp8 (3 significand bits).
+//
+// MFMA operands (32x32x16 bf16): lane l feeds 8 values of row (A) or column
+// (B) l % 32 for k = 16 s + 8 (l / 32) + j in step s; the 32x32 result sits
+// in lane l as column l % 32, rows 8 (j / 4) + 4 (l / 32) + j % 4.
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace i8h {
+
+enum class WFmt { I8, E4M3 };
+
+constexpr int kGThreads = 512;
+constexpr int kGateRows = 128;    // gate rows per unit (plus as many up rows)
+constexpr int kPassRows = 128;    // pairs per m-pass
+constexpr int kMTiles = 2;        // m-tiles of 32 per wave
+constexpr int kStageK = 64;       // K per pipeline stage
+constexpr int kSlots = 4;         // LDS ring depth (3 stages in flight)
+constexpr int kXcds = 8;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt immediates (gfx9 layout: vmcnt [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8]); unconstrained fields at their maximum
+constexpr int wait_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+template <WFmt F>
+__device__ __forceinline__ bf16x8 decode8(uint32_t lo, uint32_t hi) {
+  u32x4 p;
+  if constexpr (F == WFmt::I8) {
+    p[0] = pack_bf16x2(sbyte<0>(lo), sbyte<1>(lo));
+    p[1] = pack_bf16x2(sbyte<2>(lo), sbyte<3>(lo));
+    p[2] = pack_bf16x2(sbyte<0>(hi), sbyte<1>(hi));
+    p[3] = pack_bf16x2(sbyte<2>(hi), sbyte<3>(hi));
+  } else {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+    f2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+    f2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+    f2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+    p[0] = pack_bf16x2(a[0], a[1]);
+    p[1] = pack_bf16x2(b[0], b[1]);
+    p[2] = pack_bf16x2(c[0], c[1]);
+    p[3] = pack_bf16x2(d[0], d[1]);
+  }
+  return __builtin_bit_cast(bf16x8, p);
+}
+
+// The LDS ring: one array per slot, so the compiler can tell that a DMA in
+// flight to one slot does not alias the reads of another (with a single
+// indexed array it waits for every copy before any LDS read).
+__shared__ __attribute__((aligned(16))) uint16_t gA0[kPassRows * kStageK];
+__shared__ __attribute__((aligned(16))) uint16_t gA1[kPassRows * kStageK];
+__shared__ __attribute__((aligned(16))) uint16_t gA2[kPassRows * kStageK];
+__shared__ __attribute__((aligned(16))) uint16_t gA3[kPassRows * kStageK];
+__shared__ __attribute__((aligned(16))) uint8_t gB0[2 * kGateRows * kStageK];
+__shared__ __attribute__((aligned(16))) uint8_t gB1[2 * kGateRows * kStageK];
+__shared__ __attribute__((aligned(16))) uint8_t gB2[2 * kGateRows * kStageK];
+__shared__ __attribute__((aligned(16))) uint8_t gB3[2 * kGateRows * kStageK];
+// per-group side data, copied with the second (odd) stage of the group into
+// the slot of that stage: int8 -> the dword holding the bf16 scale of each of
+// the unit's 256 code rows; E4M3 -> 128 float row factors, then the dwords
+// holding the block scales of the 4 column slices (gate, up)
+__shared__ __attribute__((aligned(16))) uint32_t gC1[2 * kGateRows];
+__shared__ __attribute__((aligned(16))) uint32_t gC3[2 * kGateRows];
+
+// One 16- or 4-byte copy per lane, global -> LDS (M0 = the wave's LDS base;
+// lane l's bytes land at base + size * l). Issued as inline assembly so that
+// the compiler neither waits on it nor counts it; the kernel waits with
+// explicit s_waitcnt vmcnt. M0 is not used by any other code of the kernel.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)p);
+}
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory");
+}
+
+// LDS stage layouts. A: 128 rows x 64 bf16 (128 B, 8 pieces of 16 B), piece
+// p of row r at position p ^ ((r >> 1) & 7). B: 256 rows (gate 0..127, up
+// 128..255) x 64 codes (64 B, 4 pieces), piece p at p ^ ((r >> 2) & 3).
+// (The maps are involutions: position -> piece is the same formula.)
+__device__ __forceinline__ int a_pos(int row, int piece) { return piece ^ ((row >> 1) & 7); }
+__device__ __forceinline__ int b_pos(int row, int piece) { return piece ^ ((row >> 2) & 3); }
+
+template <WFmt F>
+__global__ void __launch_bounds__(kGThreads)
+k_gateup_gemm(const uint16_t* __restrict__ xa, const float* __restrict__ sx, int K,
+              const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int E, int N, int k,
+              const int32_t* __restrict__ expert_off, const int32_t* __restrict__ sorted_pairs,
+              float* __restrict__ gu, float* __restrict__ act, int ntiles) {
+  // unit: the units of expert e run on XCD e % 8, consecutive in dispatch order
+  const int blk = blockIdx.x;
+  const int slot = blk / kXcds;
+  const int e = (blk % kXcds) + kXcds * (slot / ntiles);
+  const int nt = slot % ntiles;
+  if (e >= E) return;
+  const int r0 = expert_off[e];
+  const int m_e = expert_off[e + 1] - r0;
+  if (m_e <= 0) return;
+
+  const int I = N / 2, G = K / kGroup, NB = N / kGroup;
+  const int S = 2 * G;                           // stages per pass
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int col = lane % 32, half = lane / 32;
+  const int ns = wave % 4;                       // column slice of this wave
+  const int i0 = nt * kGateRows + 32 * ns;
+  const int mw = 64 * (wave / 4);                // first pass row of this wave
+  const bool live = i0 < I;                      // I % 32 == 0: a live wave has all 32 rows
+  const int rg = 32 * ns + col, ru = kGateRows + 32 * ns + col;  // this lane's code rows in a B stage
+
+  // code rows this lane copies: instruction q fills B rows 16 (2 wave + q) ..
+  // +15; lane l takes row R + l / 4 and LDS position l % 4. Rows past I
+  // repeat row 0 of the expert (never used).
+  size_t bsrc[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = 16 * (2 * wave + q) + lane / 4;
+    const int gi = nt * kGateRows + (row % kGateRows);
+    const int n = gi < I ? (row < kGateRows ? gi : I + gi) : 0;
+    bsrc[q] = ((size_t)e * N + n) * K + 16 * b_pos(row, lane % 4);
+  }
+  // side data copied by this lane with the odd stage of group g (dword of
+  // element index base + g; the wanted bf16 is its half (base + g) & 1):
+  //   int8, waves 0..3: the scale of code row 64 wave + lane of the unit
+  //   E4M3, wave 2: block scale (lane % 2: gate, up) of column slice lane / 2 % 4
+  int64_t cbase = 0;  // element index at group 0
+  if constexpr (F == WFmt::I8) {
+    const int row = 64 * (wave & 3) + lane;
+    const int gi = nt * kGateRows + (row % kGateRows);
+    const int n = gi < I ? (row < kGateRows ? gi : I + gi) : 0;
+    cbase = ((int64_t)e * N + n) * G;
+  } else {
+    const int sl = (lane / 2) % 4, up = lane % 2;
+    const int gi = nt * kGateRows + 32 * sl;
+    const int nb = gi < I ? (up ? (I + gi) / kGroup : gi / kGroup) : 0;
+    cbase = ((int64_t)e * NB + nb) * G;
+  }
+  // parity of the element index (at group 0) of the scales this lane reads
+  // back in the fold: which half of the copied dword holds the bf16
+  int par_g, par_u;
+  if constexpr (F == WFmt::I8) {
+    par_g = (int)((((int64_t)e * N + (live ? i0 + col : 0)) * G) & 1);
+    par_u = (int)((((int64_t)e * N + (live ? I + i0 + col : 0)) * G) & 1);
+  } else {
+    par_g = (int)((((int64_t)e * NB + (live ? i0 / kGroup : 0)) * G) & 1);
+    par_u = (int)((((int64_t)e * NB + (live ? (I + i0) / kGroup : 0)) * G) & 1);
+  }
+
+  for (int mb = 0; mb < m_e; mb += kPassRows) {
+    const int rows = min(kPassRows, m_e - mb);
+    const bool busy = live && rows > mw;         // the wave has live rows in this pass
+    // activation rows this lane copies: instruction q fills A rows
+    // 8 (2 wave + q) .. +7; lane l takes row R + l / 8 and LDS position l % 8.
+    // Rows past the pass repeat the last valid row (their results are never stored).
+    int asrc[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int row = 8 * (2 * wave + q) + lane / 8;
+      const int t = sorted_pairs[r0 + mb + min(row, rows - 1)] / k;
+      asrc[q] = t * K + 8 * a_pos(row, lane % 8);
+    }
+    int xrow_tok = 0;                            // E4M3, waves 0, 1: token of pass row 64 wave + lane
+    if constexpr (F == WFmt::E4M3) {
+      const int row = 64 * (wave & 1) + lane;
+      xrow_tok = sorted_pairs[r0 + mb + min(row, rows - 1)] / k;
+    }
+
+    // stage h = (group h / 2, K half h % 2) into the given ring slot; the odd
+    // stage of a group also brings the group's side data
+    auto issue = [&](int h, uint16_t* aslot, uint8_t* bslot, uint32_t* cslot) {
+      const int koff = h * kStageK;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        dma16(xa + asrc[q] + koff, lds_addr(&aslot[8 * (2 * wave + q) * kStageK]));
+        dma16(codes + bsrc[q] + koff, lds_addr(&bslot[16 * (2 * wave + q) * kStageK]));
+      }
+      if (h & 1) {
+        const int g = h / 2;
+        if constexpr (F == WFmt::I8) {
+          if (wave < 4) dma4(scales + ((cbase + g) & ~(int64_t)1), lds_addr(&cslot[64 * wave]));
+        } else {
+          if (wave < 2) dma4(sx + (size_t)xrow_tok * G + g, lds_addr(&cslot[64 * wave]));
+          else if (wave == 2) dma4(scales + ((cbase + g) & ~(int64_t)1), lds_addr(&cslot[2 * kGateRows / 2]));
+        }
+      }
+    };
+
+    f32x16 acc[kMTiles][2], tmp[kMTiles][2];
+#pragma unroll
+    for (int a = 0; a < kMTiles; ++a)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          acc[a][c][j] = 0.0f;
+          tmp[a][c][j] = 0.0f;
+        }
+
+    auto half_bf16 = [](uint32_t w, int odd) { return __uint_as_float(odd ? (w & 0xffff0000u) : (w << 16)); };
+
+    auto stage = [&](int h, const uint16_t* abuf, const uint8_t* bbuf, const uint32_t* cbuf,
+                     uint16_t* anext, uint8_t* bnext, uint32_t* cnext) {
+      if (h >= S) return;
+      const int g = h / 2, hh = h % 2;
+      // wait for this wave's copies of stage h: the copies of the stages issued
+      // after it (4 each, plus side data) may stay in flight
+      const int later = min(2, S - 1 - h);
+      if (later == 2) __builtin_amdgcn_s_waitcnt(wait_vm(8));
+      else if (later == 1) __builtin_amdgcn_s_waitcnt(wait_vm(4));
+      else __builtin_amdgcn_s_waitcnt(wait_vm(0));
+      __builtin_amdgcn_s_barrier();            // ... and every other wave's
+      if (h + 3 < S) issue(h + 3, anext, bnext, cnext);  // the slot of stage h - 1, now free
+      if (!busy) return;
+      if (hh == 0) {
+#pragma unroll
+        for (int a = 0; a < kMTiles; ++a)
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) tmp[a][c][j] = 0.0f;
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x2 cgw = *reinterpret_cast<const u32x2*>(&bbuf[rg * kStageK + 16 * b_pos(rg, s) + 8 * half]);
+        const u32x2 cuw = *reinterpret_cast<const u32x2*>(&bbuf[ru * kStageK + 16 * b_pos(ru, s) + 8 * half]);
+        const bf16x8 wg = decode8<F>(cgw[0], cgw[1]);
+        const bf16x8 wu = decode8<F>(cuw[0], cuw[1]);
+#pragma unroll
+        for (int a = 0; a < kMTiles; ++a) {
+          const int m = mw + 32 * a + col;
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(&abuf[m * kStageK + 8 * a_pos(m, 2 * s + half)]);
+          tmp[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, wg, tmp[a][0], 0, 0, 0);
+          tmp[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, wu, tmp[a][1], 0, 0, 0);
+        }
+      }
+      if (hh == 1) {
+        if constexpr (F == WFmt::I8) {
+          const float sg = half_bf16(cbuf[rg], (par_g + g) & 1), su = half_bf16(cbuf[ru], (par_u + g) & 1);
+#pragma unroll
+          for (int a = 0; a < kMTiles; ++a)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              acc[a][0][j] = fmaf(tmp[a][0][j], sg, acc[a][0][j]);
+              acc[a][1][j] = fmaf(tmp[a][1][j], su, acc[a][1][j]);
+            }
+        } else {
+          const float wg = half_bf16(cbuf[kGateRows + 2 * ns], (par_g + g) & 1);
+          const float wu = half_bf16(cbuf[kGateRows + 2 * ns + 1], (par_u + g) & 1);
+#pragma unroll
+          for (int a = 0; a < kMTiles; ++a)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const float f = __uint_as_float(cbuf[mw + 32 * a + 8 * (j / 4) + 4 * half + (j % 4)]);
+              acc[a][0][j] = fmaf(tmp[a][0][j], wg * f, acc[a][0][j]);
+              acc[a][1][j] = fmaf(tmp[a][1][j], wu * f, acc[a][1][j]);
+            }
+        }
+      }
+    };
+
+    __builtin_amdgcn_s_barrier();  // nobody still reads the ring of the previous pass
+    issue(0, gA0, gB0, nullptr);
+    if (S > 1) issue(1, gA1, gB1, gC1);
+    if (S > 2) issue(2, gA2, gB2, nullptr);
+    for (int hb = 0; hb < S; hb += kSlots) {     // stage h uses slot h % 4, fixed at compile time
+      stage(hb + 0, gA0, gB0, nullptr, gA3, gB3, gC3);
+      stage(hb + 1, gA1, gB1, gC1, gA0, gB0, nullptr);
+      stage(hb + 2, gA2, gB2, nullptr, gA1, gB1, gC1);
+      stage(hb + 3, gA3, gB3, gC3, gA2, gB2, nullptr);
+    }
+    if (busy) {
+#pragma unroll
+      for (int a = 0; a < kMTiles; ++a) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int m = mw + 32 * a + 8 * (j / 4) + 4 * half + (j % 4);
+          if (m < rows) {
+            const size_t r = (size_t)(r0 + mb + m);
+            const float gv = acc[a][0][j], uv = acc[a][1][j];
+            if (gu) {
+              gu[r * N + i0 + col] = gv;
+              gu[r * N + I + i0 + col] = uv;
+            }
+            if (act) act[r * I + i0 + col] = gelu_tanh(gv) * uv;
+          }
+        }
+      }
+    }
+  }
+}
+
+static int gemm_grid(int E, int ntiles) { return cdiv(E, kXcds) * kXcds * ntiles; }
+
+hipError_t launch_gateup_i8h_gemm(const uint16_t* xrot, int T, int K, const int8_t* codes,
+                                  const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
+                                  const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st) {
+  (void)T;
+  int ntiles = cdiv(N / 2, kGateRows);
+  k_gateup_gemm<WFmt::I8><<<gemm_grid(E, ntiles), kGThreads, 0, st>>>(
+      xrot, nullptr, K, reinterpret_cast<const uint8_t*>(codes), scales, E, N, k, expert_off, sorted_pairs, gu,
+      act, ntiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup_fp8(const uint16_t* xq, const float* sx, int T, int K, const uint8_t* codes,
+                             const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
+                             const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st) {
+  (void)T;
+  int ntiles = cdiv(N / 2, kGateRows);
+  k_gateup_gemm<WFmt::E4M3><<<gemm_grid(E, ntiles), kGThreads, 0, st>>>(
+      xq, sx, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu, act, ntiles);
+  return hipGetLastError();
+}
+
+}  // namespace i8h

@@ -17,11 +17,20 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "xlane.hpp"
 
 namespace i8h {
 
 constexpr int kChunkPairs = 256;   // pairs per histogram/scatter block
 constexpr int kRouteThreads = 256;
+
+// Keep the better of this lane's and its xor-M partner's candidate.
+template <int M>
+__device__ __forceinline__ void best_step(float& bv, int& bi) {
+  float ov = xor_lane<M>(bv);
+  int oi = xor_lane_i<M>(bi);
+  if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+}
 
 // --- top-k of one token, by one wave ------------------------------------
 // Lane l holds logits e = l + 64 v. Each round takes the wave-wide best
@@ -51,12 +60,12 @@ __device__ __forceinline__ void topk_one_token(const float* __restrict__ row, in
     }
     // wave-wide best: larger value first, then lower index (a total order,
     // so every lane ends with the same winner)
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      float ov = __shfl_xor(bv, m, kWave);
-      int oi = __shfl_xor(bi, m, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
+    best_step<1>(bv, bi);
+    best_step<2>(bv, bi);
+    best_step<4>(bv, bi);
+    best_step<8>(bv, bi);
+    best_step<16>(bv, bi);
+    best_step<32>(bv, bi);
     if ((bi % kWave) == lane) retired |= 1u << (bi / kWave);
     if (lane == j) { my_id = bi; my_logit = bv; }
   }

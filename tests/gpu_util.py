@@ -68,8 +68,12 @@ def near_tie_mask(exact, window):
 
 def check_rotation(x_bits, y_bits):
     """GPU rotation y (bf16 bits) of x (bf16 bits) against the oracle: equal
-    everywhere except at proven near-ties, where the two results must be
-    adjacent bf16 values. Returns the number of near-tie differences."""
+    everywhere except where the float32 evaluation may legitimately round
+    differently. The GPU value is the bf16 rounding of a float32 result within
+    `fwht_tie_window` of the exact value, so any difference must satisfy
+    |gpu - exact| <= window + half a bf16 step, and the exact value must lie
+    within the window of a rounding midpoint. Returns the number of
+    differences."""
     x = numfmt.bf16_from_bits(x_bits)
     exact = hadamard.rotate_blocks(x)
     want = numfmt.bf16_round(exact)
@@ -80,8 +84,8 @@ def check_rotation(x_bits, y_bits):
     win = fwht_tie_window(x)
     tie = near_tie_mask(exact, win)
     assert np.all(tie[diff]), f"{(diff & ~tie).sum()} differences away from any rounding tie"
-    gb = numfmt.bf16_to_bits(got[diff]).astype(np.int64)
-    wb = numfmt.bf16_to_bits(want[diff]).astype(np.int64)
-    # adjacent bf16 values: bit patterns differ by one (same sign), or +-0 vs smallest
-    assert np.all(np.abs(gb - wb) == 1), "a near-tie difference larger than one bf16 step"
+    mag = np.maximum(np.abs(got), np.abs(exact))[diff]
+    half = np.ldexp(1.0, np.frexp(mag + 1e-300)[1] - 9)
+    err = np.abs(got - exact)[diff]
+    assert np.all(err <= win[diff] + half), "a difference beyond the float32 error bound"
     return int(diff.sum())

@@ -33,7 +33,7 @@ def L():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -50,8 +50,10 @@ def test_workspace_sizes(L):
     assert L.moe_route_permute_workspace_size(1, 128, 8) == 0          # single-block path
     assert L.moe_route_permute_workspace_size(2048, 128, 8) == 64 * 128 * 4
     assert L.moe_route_permute_workspace_size(0, 128, 8) == 0
-    assert L.moe_gateup_fp8blk_workspace_size(128, 2048) == 128 * 2048 + 128 * 16 * 4
-    assert L.moe_gateup_fp8blk_workspace_size(3, 128) == 512 + 256    # each part rounded to 256 B
+    assert L.moe_gateup_fp8blk_workspace_size(128, 2048) == 128 * 2048 + 128 * 16 * 4 + 128 * 2048 * 2
+    assert L.moe_gateup_fp8blk_workspace_size(3, 128) == 512 + 256 + 768   # each part rounded to 256 B
+    assert L.moe_gateup_i8h_fused_workspace_size(1, 2048) == 0          # rotation inside the decode kernel
+    assert L.moe_gateup_i8h_fused_workspace_size(128, 2048) == 128 * 2048 * 2
 
 
 def route(L, T=8, E=16, k=2, ptr=A, ws=A, wsb=1 << 20):
@@ -108,6 +110,15 @@ def test_gateup_i8h_validation(L):
     assert gemm(L, gu=None, act=None) == OK          # nothing requested
     assert gemm(L, K=8192, path=1) == EUNSUP         # decode kernel keeps K <= 4096
     assert L.moe_gateup_i8h_grouped(None, 4, 256, A, A, 8, 256, 2, A, A, A, A, None) == EINVAL
+
+
+def test_fused_validation(L):
+    f = L.moe_gateup_i8h_grouped_fused
+    assert f(A, 4, 100, A, A, 8, 256, 2, A, A, A, A, None, 0, None) == EINVAL
+    assert f(A, 100, 256, A, A, 8, 256, 2, A, A, A, A, None, 0, None) == EINVAL     # workspace needed
+    assert f(A, 100, 256, A, A, 8, 256, 2, A, A, A, A, A, 16, None) == EINVAL       # too small
+    assert f(A, 0, 256, A, A, 8, 256, 2, A, A, A, A, None, 0, None) == OK
+    assert f(A, 1 << 20, 4096, A, A, 8, 256, 2, A, A, A, A, A, 1 << 40, None) == EUNSUP  # T*K overflows
 
 
 def test_fp8_validation(L):

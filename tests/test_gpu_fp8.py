@@ -79,8 +79,11 @@ def _run(L, codes, sbits, rows=None, what=""):
     torch.cuda.synchronize()
     qx, sx = quant.quantize_fp8_activations(synth.bf16_bits_to_f64(xb))
     # the workspace keeps the quantized activations: bit-exact
-    gq, gs = i8h.fp8_workspace_views(ws, L.T, L.K)
+    gq, gs, gx = i8h.fp8_workspace_views(ws, L.T, L.K)
     assert np.array_equal(gq.cpu().numpy(), qx) and np.array_equal(gs.cpu().numpy(), sx)
+    # the exact bf16 values of the codes, as the product consumes them
+    xq = gx.float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(xq, numfmt.e4m3_decode(qx))
     ref = gateup.gateup_fp8blk(qx, sx, codes, numfmt.bf16_from_bits(sbits), r["expert_off"], r["sorted_pairs"],
                                L.topk, rows=rows)
     sel = slice(None) if rows is None else rows
