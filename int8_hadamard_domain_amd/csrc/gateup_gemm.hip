@@ -140,13 +140,18 @@ k_gateup_gemm(const uint16_t* __restrict__ xa, const float* __restrict__ sx, int
 
   const int I = N / 2, G = K / kGroup, NB = N / kGroup;
   const int S = 2 * G;                           // stages per pass
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: kept in a scalar register
   const int col = lane % 32, half = lane / 32;
   const int ns = wave % 4;                       // column slice of this wave
   const int i0 = nt * kGateRows + 32 * ns;
   const int mw = 64 * (wave / 4);                // first pass row of this wave
   const bool live = i0 < I;                      // I % 32 == 0: a live wave has all 32 rows
   const int rg = 32 * ns + col, ru = kGateRows + 32 * ns + col;  // this lane's code rows in a B stage
+  // LDS byte addresses of the ring (scalar, computed once)
+  const uint32_t la0 = lds_addr(gA0), la1 = lds_addr(gA1), la2 = lds_addr(gA2), la3 = lds_addr(gA3);
+  const uint32_t lb0 = lds_addr(gB0), lb1 = lds_addr(gB1), lb2 = lds_addr(gB2), lb3 = lds_addr(gB3);
+  const uint32_t lc1 = lds_addr(gC1), lc3 = lds_addr(gC3);
 
   // code rows this lane copies: instruction q fills B rows 16 (2 wave + q) ..
   // +15; lane l takes row R + l / 4 and LDS position l % 4. Rows past I
@@ -205,22 +210,23 @@ k_gateup_gemm(const uint16_t* __restrict__ xa, const float* __restrict__ sx, int
       xrow_tok = sorted_pairs[r0 + mb + min(row, rows - 1)] / k;
     }
 
-    // stage h = (group h / 2, K half h % 2) into the given ring slot; the odd
-    // stage of a group also brings the group's side data
-    auto issue = [&](int h, uint16_t* aslot, uint8_t* bslot, uint32_t* cslot) {
+    // stage h = (group h / 2, K half h % 2) into the given ring slot (LDS byte
+    // addresses of its A, B and side arrays); the odd stage of a group also
+    // brings the group's side data
+    auto issue = [&](int h, uint32_t aslot, uint32_t bslot, uint32_t cslot) {
       const int koff = h * kStageK;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        dma16(xa + asrc[q] + koff, lds_addr(&aslot[8 * (2 * wave + q) * kStageK]));
-        dma16(codes + bsrc[q] + koff, lds_addr(&bslot[16 * (2 * wave + q) * kStageK]));
+        dma16(xa + asrc[q] + koff, aslot + (2 * wave + q) * (8 * kStageK * 2));
+        dma16(codes + bsrc[q] + koff, bslot + (2 * wave + q) * (16 * kStageK));
       }
       if (h & 1) {
         const int g = h / 2;
         if constexpr (F == WFmt::I8) {
-          if (wave < 4) dma4(scales + ((cbase + g) & ~(int64_t)1), lds_addr(&cslot[64 * wave]));
+          if (wave < 4) dma4(scales + ((cbase + g) & ~(int64_t)1), cslot + 64 * 4 * wave);
         } else {
-          if (wave < 2) dma4(sx + (size_t)xrow_tok * G + g, lds_addr(&cslot[64 * wave]));
-          else if (wave == 2) dma4(scales + ((cbase + g) & ~(int64_t)1), lds_addr(&cslot[2 * kGateRows / 2]));
+          if (wave < 2) dma4(sx + (size_t)xrow_tok * G + g, cslot + 64 * 4 * wave);
+          else if (wave == 2) dma4(scales + ((cbase + g) & ~(int64_t)1), cslot + 4 * kGateRows);
         }
       }
     };
@@ -239,7 +245,7 @@ k_gateup_gemm(const uint16_t* __restrict__ xa, const float* __restrict__ sx, int
     auto half_bf16 = [](uint32_t w, int odd) { return __uint_as_float(odd ? (w & 0xffff0000u) : (w << 16)); };
 
     auto stage = [&](int h, const uint16_t* abuf, const uint8_t* bbuf, const uint32_t* cbuf,
-                     uint16_t* anext, uint8_t* bnext, uint32_t* cnext) {
+                     uint32_t anext, uint32_t bnext, uint32_t cnext) {
       if (h >= S) return;
       const int g = h / 2, hh = h % 2;
       // wait for this wave's copies of stage h: the copies of the stages issued
@@ -299,14 +305,14 @@ k_gateup_gemm(const uint16_t* __restrict__ xa, const float* __restrict__ sx, int
     };
 
     __builtin_amdgcn_s_barrier();  // nobody still reads the ring of the previous pass
-    issue(0, gA0, gB0, nullptr);
-    if (S > 1) issue(1, gA1, gB1, gC1);
-    if (S > 2) issue(2, gA2, gB2, nullptr);
+    issue(0, la0, lb0, 0);
+    if (S > 1) issue(1, la1, lb1, lc1);
+    if (S > 2) issue(2, la2, lb2, 0);
     for (int hb = 0; hb < S; hb += kSlots) {     // stage h uses slot h % 4, fixed at compile time
-      stage(hb + 0, gA0, gB0, nullptr, gA3, gB3, gC3);
-      stage(hb + 1, gA1, gB1, gC1, gA0, gB0, nullptr);
-      stage(hb + 2, gA2, gB2, nullptr, gA1, gB1, gC1);
-      stage(hb + 3, gA3, gB3, gC3, gA2, gB2, nullptr);
+      stage(hb + 0, gA0, gB0, nullptr, la3, lb3, lc3);
+      stage(hb + 1, gA1, gB1, gC1, la0, lb0, 0);
+      stage(hb + 2, gA2, gB2, nullptr, la1, lb1, lc1);
+      stage(hb + 3, gA3, gB3, gC3, la2, lb2, 0);
     }
     if (busy) {
 #pragma unroll
