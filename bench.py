@@ -5,7 +5,8 @@ One step = one pass of the whole path over one batch of tokens of a routed-
 expert gate_up layer (Gemma 4 26B-A4B shapes: hidden 2048, 128 experts,
 top-8, 2 x 768 gate_up rows per expert):
     moe_route_permute -> hadamard128_rotate -> moe_gateup_i8h_grouped (act out)
-or, for the FP8 block variant, moe_route_permute -> moe_gateup_fp8blk_grouped.
+For a few tokens the three run as one launch (moe_route_gateup_i8h_decode);
+for the FP8 block variant the step is moe_route_permute -> moe_gateup_fp8blk_grouped.
 
 Default workload: one decode token (T = 1). Inputs are seeded synthetic data
 already resident in HBM; every step takes a different token (router logits
@@ -46,6 +47,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
+    ap.add_argument("--two-launch", action="store_true",
+                    help="decode: time moe_route_permute + moe_gateup_i8h_grouped_fused instead of the "
+                         "one-launch moe_route_gateup_i8h_decode")
     ap.add_argument("--unfused", action="store_true",
                     help="rotate with hadamard128_rotate, then moe_gateup_i8h_grouped (default for decode: "
                          "moe_gateup_i8h_grouped_fused, rotation inside the gate_up kernel)")
@@ -74,6 +78,7 @@ def main():
     L = synth.layer(name)
     fp8 = name == "fp8"
     fused = (not fp8) and (not args.unfused) and args.path == "auto" and L.T <= 8
+    one_launch = fused and not args.two_launch and L.P <= 64 and L.E <= 256 and L.K <= 4096
     per_copy_bytes = L.E * L.N * L.K * (1 + (2 / (128 * 128) if fp8 else 2 / 128))
     if args.copies > 0:
         copies = args.copies
@@ -122,7 +127,10 @@ def main():
     def gate_up(i):
         b = route_bufs[i]
         c = i % copies
-        if fp8:
+        if one_launch:
+            i8h.moe_route_gateup_i8h_decode(logits[i % nb], xs[i % nb], codes[c], scales[c], k, gate_up=False,
+                                            act=act, out=b)
+        elif fp8:
             i8h.moe_gateup_fp8blk_grouped(xs[i % nb], codes[c], scales[c], k, b["expert_off"], b["sorted_pairs"],
                                           gate_up=False, act=act, workspace=fp8_ws)
         elif fused:
@@ -133,6 +141,9 @@ def main():
                                        gate_up=False, act=act, path=args.path)
 
     def step(i):
+        if one_launch:           # routing is inside the kernel
+            gate_up(i)
+            return
         i8h.moe_route_permute(logits[i % nb], k, out=route_bufs[i])
         if not fp8 and not fused:
             i8h.hadamard128_rotate(xs[i % nb], out=xr)
@@ -196,11 +207,16 @@ def main():
     # act written, routing lists read
     x_bytes = L.T * L.K * (1 if fp8 else 2)
     alg_bytes = weight_bytes.mean() + x_bytes + L.P * (L.N // 2) * 4 + L.P * 4 + (L.E + 1) * 4
+    if one_launch:
+        # the kernel also reads the logits and writes ids, weights and pair_pos
+        alg_bytes += L.T * L.E * 4 + 3 * L.P * 4
     if fp8:
         alg_bytes += L.T * L.K * 2 + L.T * L.G * 4       # quantizer reads bf16 x, writes scales
     achieved = alg_bytes / (kern_us * 1e-6) / 1e9
     flops = 2.0 * L.P * L.N * L.K
-    if fp8:
+    if one_launch:
+        kernel_name = "k_route_gateup_decode (routing + rotation + gate_up)"
+    elif fp8:
         kernel_name = "k_gateup_gemm<E4M3> (+ k_fp8_act_quant)"
     elif args.path == "gemv" or (args.path == "auto" and L.T <= 8):
         kernel_name = "k_gateup_i8h_gemv" + ("<rotation fused>" if fused else "")
@@ -234,7 +250,8 @@ def main():
                    "T": L.T, "K": L.K, "E": L.E, "topk": k, "N": L.N, "weight_copies": int(copies),
                    "steps_per_graph": int(S), "touched_experts_per_step": float(np.mean(touched)),
                    "outputs": "act (fp32); gate_up not stored", "setup_s": round(setup_s, 1),
-                   "step": ("route -> gate_up (FP8 quantizer + product)" if fp8 else
+                   "step": ("route -> rotate -> gate_up in one launch" if one_launch else
+                            "route -> gate_up (FP8 quantizer + product)" if fp8 else
                             "route -> gate_up with the rotation fused" if fused else
                             "route -> rotate -> gate_up")},
         "roofline": roofline,

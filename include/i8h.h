@@ -159,6 +159,21 @@ int moe_gateup_i8h_grouped_fused(const uint16_t* x, int T, int K,
                                  float* gate_up, float* act,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode step in one launch: moe_route_permute, then
+ * moe_gateup_i8h_grouped_fused, for a few tokens. Each workgroup ranks the
+ * logits of every token itself and picks its expert from the result, so the
+ * code stream starts without waiting for a routing kernel; one workgroup also
+ * stores the routing outputs. Same inputs, outputs and rules as those two
+ * calls (x is the UNROTATED activation), with the same bit-exact routing;
+ * no workspace. Limits (else I8H_EUNSUPPORTED): T*topk <= 64, E <= 256,
+ * K <= 4096. Needs at least one of gate_up and act; N % 64 == 0. */
+int moe_route_gateup_i8h_decode(const float* logits, const uint16_t* x, int T, int K,
+                                const int8_t* codes, const uint16_t* scales,
+                                int E, int N, int topk,
+                                int32_t* topk_ids, float* topk_w, int32_t* expert_off,
+                                int32_t* sorted_pairs, int32_t* pair_pos,
+                                float* gate_up, float* act, void* stream);
+
 /* ------------------------------------------------------------------------
  * FP8 activation quantizer: per token and per 128 of K (one float32 scale
  * per token and 128 values, as the activations of the int8 12B card, header
@@ -181,7 +196,7 @@ int fp8_quantize_activations(const uint16_t* x, int T, int K,
  * with the same epilogue, row order and outputs as moe_gateup_i8h_grouped.
  *
  * x [T, K] bf16; codes [E, N, K] E4M3FN bytes (finite); scales [E, N/128,
- * K/128] bf16; N must be a positive multiple of 128 (whole 128-row scale
+ * K/128] bf16, 4-byte aligned; N must be a positive multiple of 128 (whole 128-row scale
  * blocks). The products of decoded codes are exact and summed in float32
  * (the codes are expanded to bf16 for bf16 MFMA; gfx950's FP8 MFMA keeps
  * only about 13 bits below its largest product). Workspace (at least

@@ -11,6 +11,7 @@ Functions (same names as the C entry points):
   hadamard128_rotate         blockwise 128-wide Walsh-Hadamard rotation (bf16)
   moe_gateup_i8h_grouped     grouped int8 Hadamard-domain gate_up + GELU epilogue
   moe_gateup_i8h_grouped_fused  the same on unrotated activations (rotation fused)
+  moe_route_gateup_i8h_decode   routing + rotation + gate_up in one launch (few tokens)
   fp8_quantize_activations   per-token, per-128 E4M3 activation quantizer
   moe_gateup_fp8blk_grouped  grouped FP8 E4M3 128x128-block gate_up + epilogue
 """
@@ -55,6 +56,7 @@ def lib():
         "moe_gateup_i8h_grouped_path": (I, [P, I, I, P, P, I, I, I, P, P, P, P, I, P]),
         "moe_gateup_i8h_fused_workspace_size": (SZ, [I, I]),
         "moe_gateup_i8h_grouped_fused": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P, SZ, P]),
+        "moe_route_gateup_i8h_decode": (I, [P, P, I, I, P, P, I, I, I, P, P, P, P, P, P, P, P]),
         "fp8_quantize_activations": (I, [P, I, I, P, P, P]),
         "moe_gateup_fp8blk_workspace_size": (SZ, [I, I]),
         "moe_gateup_fp8blk_grouped": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P, SZ, P]),
@@ -185,6 +187,37 @@ def moe_gateup_i8h_grouped_fused(x, codes, scales, topk, expert_off, sorted_pair
         _ptr(gu), _ptr(ac), _ptr(workspace) if need > 0 else None, 0 if workspace is None else workspace.numel(),
         _stream(dev)))
     return gu, ac
+
+
+def moe_route_gateup_i8h_decode(logits, x, codes, scales, topk, gate_up=True, act=True, out=None):
+    """Decode step in one launch: moe_route_permute on logits [T, E] float32,
+    then the fused-rotation gate_up on UNROTATED x [T, K] bf16 (T*topk <= 64,
+    E <= 256, K <= 4096). Returns (routing dict as moe_route_permute's,
+    gate_up, act). `out` may hold preallocated routing tensors."""
+    _dev(logits, "logits", torch.float32, 2)
+    _dev(x, "x", torch.bfloat16, 2)
+    _dev(codes, "codes", torch.int8, 3)
+    _dev(scales, "scales", torch.bfloat16, 3)
+    T, E = logits.shape
+    T2, K = x.shape
+    E2, N, K2 = codes.shape
+    if T2 != T or E2 != E or K2 != K or scales.shape != (E, N, K // 128):
+        raise ValueError("inconsistent shapes")
+    dev = x.device
+    o = dict(out or {})
+    i32 = dict(dtype=torch.int32, device=dev)
+    o.setdefault("topk_ids", torch.empty((T, topk), **i32))
+    o.setdefault("topk_w", torch.empty((T, topk), dtype=torch.float32, device=dev))
+    o.setdefault("expert_off", torch.empty((E + 1,), **i32))
+    o.setdefault("sorted_pairs", torch.empty((T * topk,), **i32))
+    o.setdefault("pair_pos", torch.empty((T * topk,), **i32))
+    gu = _out(gate_up, (T * topk, N), dev)
+    ac = _out(act, (T * topk, N // 2), dev)
+    _check("moe_route_gateup_i8h_decode", lib().moe_route_gateup_i8h_decode(
+        _ptr(logits), _ptr(x), T, K, _ptr(codes), _ptr(scales), E, N, topk, _ptr(o["topk_ids"]),
+        _ptr(o["topk_w"]), _ptr(o["expert_off"]), _ptr(o["sorted_pairs"]), _ptr(o["pair_pos"]),
+        _ptr(gu), _ptr(ac), _stream(dev)))
+    return o, gu, ac
 
 
 def _out(spec, shape, dev):

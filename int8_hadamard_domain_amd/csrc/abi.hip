@@ -13,6 +13,8 @@ using i8h::kMaxTopk;
 
 constexpr int kGemvMaxK = 4096;   // the decode kernel keeps K/1024 pieces per lane
 constexpr int kGemvMaxT = 8;      // AUTO picks the decode kernel up to this many tokens
+constexpr int kDecodeMaxPairs = 64;     // the fused decode kernel groups all pairs in one wave
+constexpr int kDecodeMaxExperts = 256;  // ... and ranks at most 4 logits per lane
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -174,6 +176,28 @@ int moe_gateup_i8h_grouped_fused(const uint16_t* x, int T, int K, const int8_t* 
   if (i8h::launch_fwht128(x, K, xr, K, T, K, st) != hipSuccess) return I8H_EHIP;
   return from_hip(i8h::launch_gateup_i8h_gemm(xr, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs,
                                                gate_up, act, st));
+}
+
+int moe_route_gateup_i8h_decode(const float* logits, const uint16_t* x, int T, int K, const int8_t* codes,
+                                const uint16_t* scales, int E, int N, int topk, int32_t* topk_ids, float* topk_w,
+                                int32_t* expert_off, int32_t* sorted_pairs, int32_t* pair_pos, float* gate_up,
+                                float* act, void* stream) {
+  int rc = check_common_moe(T, K, E, N, topk);
+  if (rc != I8H_OK) return rc;
+  if ((N % 64) != 0) return I8H_EINVAL;
+  if ((int64_t)T * topk > kDecodeMaxPairs || E > kDecodeMaxExperts || K > kGemvMaxK) return I8H_EUNSUPPORTED;
+  if (T == 0) return I8H_OK;
+  if (!logits || !x || !codes || !scales || !topk_ids || !topk_w || !expert_off || !sorted_pairs || !pair_pos)
+    return I8H_EINVAL;
+  if (!gate_up && !act) return I8H_EINVAL;
+  if (!aligned(logits, 4) || !aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return I8H_EINVAL;
+  if (!aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(expert_off, 4) || !aligned(sorted_pairs, 4) ||
+      !aligned(pair_pos, 4))
+    return I8H_EINVAL;
+  if ((gate_up && !aligned(gate_up, 4)) || (act && !aligned(act, 4))) return I8H_EINVAL;
+  return from_hip(i8h::launch_route_gateup_decode(logits, x, T, K, codes, scales, E, N, topk, topk_ids, topk_w,
+                                                  expert_off, sorted_pairs, pair_pos, gate_up, act,
+                                                  as_stream(stream)));
 }
 
 int moe_gateup_fp8blk_grouped(const uint16_t* x, int T, int K, const uint8_t* codes, const uint16_t* scales, int E,

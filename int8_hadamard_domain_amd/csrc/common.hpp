@@ -38,13 +38,6 @@ __device__ __forceinline__ float sbyte(uint32_t w) {
   return (float)(int8_t)((w >> (8 * J)) & 0xffu);
 }
 
-// Wave-wide float sum with a fixed reduction tree (deterministic).
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
-}
-
 // GELU, tanh approximation: v/2 (1 + tanh(z)) with z = sqrt(2/pi)(v + 0.044715 v^3).
 // Evaluated as v / (1 + exp(-2z)), the same function written without the
 // cancellation of 1 + tanh(z) for negative z.

@@ -9,11 +9,12 @@
 // load and store), 4 blocks per wavefront. Butterflies (a, b) -> (a+b, a-b)
 // for index distance h: h = 1, 2, 4 run inside a lane; h = 8, 16, 32, 64 pair
 // lane j with lane j^1, j^2, j^4, j^8 of the same 16-lane DPP row, moved with
-// DPP quad_perm (xor 1, xor 2), ds_swizzle bit mode (xor 4) and DPP row_ror:8
-// (xor 8). All arithmetic is float32; one bf16 rounding at the end.
+// DPP (quad_perm for xor 1 and 2, row rotations for xor 4 and 8). All
+// arithmetic is float32; one bf16 rounding at the end.
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "xlane.hpp"
 
 namespace i8h {
 
@@ -21,21 +22,11 @@ constexpr int kFwhtThreads = 256;
 constexpr int kBlocksPerWg = kFwhtThreads / 16;
 
 template <int M>
-__device__ __forceinline__ float lane_xor(float v) {
-  int i = __float_as_int(v);
-  if constexpr (M == 1) i = __builtin_amdgcn_update_dpp(0, i, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
-  else if constexpr (M == 2) i = __builtin_amdgcn_update_dpp(0, i, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
-  else if constexpr (M == 4) i = __builtin_amdgcn_ds_swizzle(i, (4 << 10) | 0x1F);  // bit mode, xor 4
-  else i = __builtin_amdgcn_update_dpp(0, i, 0x128, 0xF, 0xF, false);                  // row_ror:8 == xor 8
-  return __int_as_float(i);
-}
-
-template <int M>
 __device__ __forceinline__ void cross_stage(float (&v)[8], int j) {
   bool upper = (j & M) != 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    float o = lane_xor<M>(v[i]);
+    float o = xor_lane<M>(v[i]);
     v[i] = upper ? (o - v[i]) : (v[i] + o);
   }
 }

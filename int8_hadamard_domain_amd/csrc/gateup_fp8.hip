@@ -23,6 +23,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "xlane.hpp"
 
 namespace i8h {
 
@@ -82,8 +83,10 @@ k_fp8_act_quant(const uint16_t* __restrict__ x, int T, int K, uint8_t* __restric
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+  amax = fmaxf(amax, xor_lane<1>(amax));
+  amax = fmaxf(amax, xor_lane<2>(amax));
+  amax = fmaxf(amax, xor_lane<4>(amax));
+  amax = fmaxf(amax, xor_lane<8>(amax));
   float s = amax / 448.0f;                   // IEEE single division
   uint32_t out0 = 0, out1 = 0;
   if (s != 0.0f) {

@@ -6,51 +6,76 @@
 //   gu[r, n] = sum_g s[e, n, g] * sum_{kk in g} q[e, n, kk] * x_rot[t, kk]
 //   act[r, i] = gelu_tanh(gu[r, i]) * gu[r, I + i]
 //
-// Work split: grid y = slot of a non-empty expert (found by scanning
-// expert_off on the device), grid x = groups of row pairs (i, I + i). Each
-// wave owns RPW row pairs and issues all of their code loads at once (lane l
-// reads the 16-byte pieces kk = 16 (l + 64 c) of every row: each wave load is
-// 1 KB of one row), so many kilobytes are in flight per wave. Codes become
-// float exactly (sign-extended byte converts), products with the bf16
-// activations are exact in float32 FMAs, each 16-value partial is scaled by
-// its group's bf16 scale, and one transposing reduction (xor 32, 16, 8 keep
-// half of the values each step; then xor 4, 2, 1) finishes all 2*RPW dot
-// products of the wave in a fixed order. The codes are read once and reused
-// for every token routed to the expert.
+// Work split: grid y = slot of a non-empty expert, grid x = groups of row
+// pairs (i, I + i). Each wave owns RPW row pairs and issues all of their code
+// loads at once (lane l reads the 16-byte pieces kk = 16 (l + 64 c) of every
+// row: each wave load is 1 KB of one row), so many kilobytes are in flight per
+// wave. Codes become float exactly (sign-extended byte converts), products
+// with the bf16 activations are exact in float32 FMAs, each 16-value partial
+// is scaled by its group's bf16 scale, and one transposing reduction (xor 32,
+// 16, 8 keep half of the values each step; then xor 4, 2, 1) finishes all
+// 2*RPW dot products of the wave in a fixed order. The codes are read once and
+// reused for every token routed to the expert.
+//
+// Latency: at decode the whole kernel is one trip to HBM, so nothing that
+// decides which codes to read may cost a trip of its own. The expert of a
+// slot comes from one batch of expert_off loads (all issued before any is
+// used) and ballots; the token of a row from a scalar load that overlaps the
+// code stream.
 //
 // ROT = true takes unrotated activations and applies the 128-wide Hadamard
 // rotation in the prologue: the 8 lanes holding one 128-block run four
 // butterfly stages in registers and three across lanes (xor 1, 2, 4), scale
 // by 1/sqrt(128) and round to bf16, exactly the activation the separate
 // rotation call would produce up to float32 rounding order.
+//
+// k_route_gateup_decode adds the router in front (few tokens, at most 64
+// pairs): every block ranks the logits of all tokens itself (a wave per
+// token), groups the pairs by expert with ballots, picks the expert of its
+// slot and goes on as above; block (0, 0) also stores the routing outputs.
+// One launch then covers route -> rotate -> gate_up, and no block waits for
+// another kernel's results.
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "topk.hpp"
 #include "xlane.hpp"
 
 namespace i8h {
 
 constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / kWave;
+constexpr int kScanChunks = 4;  // expert_off entries per lane and round trip (E <= 256 in one)
 
-// Expert owning the s-th non-empty run of expert_off (in expert order), or
-// -1. Same answer in every lane.
-__device__ __forceinline__ int nth_nonempty_expert(const int32_t* __restrict__ off, int E, int s, int lane) {
+// Expert owning the s-th non-empty run of expert_off (in expert order), with
+// its first and one-past-last sorted row, or false. Same answer in every lane.
+__device__ __forceinline__ bool nth_nonempty_expert(const int32_t* __restrict__ off, int E, int s, int lane,
+                                                    int& e, int& r0, int& r1) {
   int seen = 0;
-  for (int base = 0; base < E; base += kWave) {
-    int e = base + lane;
-    bool ne = false;
-    if (e < E) ne = off[e + 1] > off[e];
-    uint64_t m = __ballot(ne);
-    int c = __popcll(m);
-    if (s < seen + c) {
-      int want = s - seen;  // position of the wanted set bit
-      for (int i = 0; i < want; ++i) m &= m - 1;
-      return base + __ffsll((unsigned long long)m) - 1;
+  for (int base = 0; base < E; base += kScanChunks * kWave) {
+    int a[kScanChunks], b[kScanChunks];
+#pragma unroll
+    for (int c = 0; c < kScanChunks; ++c) {
+      const int x = base + kWave * c + lane;
+      a[c] = x < E ? off[x] : 0;
+      b[c] = x < E ? off[x + 1] : 0;
     }
-    seen += c;
+#pragma unroll
+    for (int c = 0; c < kScanChunks; ++c) {
+      uint64_t m = __ballot(b[c] > a[c]);
+      const int cnt = __popcll(m);
+      if (s < seen + cnt) {
+        for (int i = seen; i < s; ++i) m &= m - 1;   // drop the lower set bits
+        const int l = __ffsll((unsigned long long)m) - 1;
+        e = base + kWave * c + l;
+        r0 = __builtin_amdgcn_readlane(a[c], l);
+        r1 = __builtin_amdgcn_readlane(b[c], l);
+        return true;
+      }
+      seen += cnt;
+    }
   }
-  return -1;
+  return false;
 }
 
 // One transposing step at lane distance M over NV values: the lane with bit
@@ -91,6 +116,152 @@ __device__ __forceinline__ void rotate16(float (&xv)[16], int lane) {
   }
 }
 
+// Codes and scales of one wave's RPW row pairs, held in registers (scales as
+// their bf16 bits: converting them where they are loaded would make the wave
+// wait for the whole code stream before it can issue anything else).
+template <int NCH, int RPW>
+struct WaveRows {
+  u32x4 cg[RPW][NCH], cu[RPW][NCH];
+  uint32_t sg[RPW][NCH], su[RPW][NCH];
+};
+
+// One token row as the lane reads it: the 16 values kk = 16 (lane + 64 c) ..
+template <int NCH>
+struct XRow {
+  u32x4 a[NCH], b[NCH];
+};
+
+template <int NCH, int RPW>
+__device__ __forceinline__ void load_rows(WaveRows<NCH, RPW>& R, const int8_t* __restrict__ codes,
+                                          const uint16_t* __restrict__ scales, int e, int N, int K, int i0,
+                                          int lane) {
+  const int I = N / 2, G = K / kGroup;
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const uint16_t* srg = scales + ((size_t)e * N + i0 + j) * G;
+    const uint16_t* sru = scales + ((size_t)e * N + I + i0 + j) * G;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int g = min(16 * (lane + kWave * c), K - 16) / kGroup;
+      R.sg[j][c] = srg[g];
+      R.su[j][c] = sru[g];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const int8_t* rowg = codes + ((size_t)e * N + i0 + j) * K;
+    const int8_t* rowu = codes + ((size_t)e * N + I + i0 + j) * K;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int kk = min(16 * (lane + kWave * c), K - 16);  // pieces past K re-read the last one
+      R.cg[j][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowg + kk));
+      R.cu[j][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowu + kk));
+    }
+  }
+}
+
+template <int NCH>
+__device__ __forceinline__ void load_x(XRow<NCH>& X, const uint16_t* __restrict__ xr, int K, int lane) {
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int kk = min(16 * (lane + kWave * c), K - 16);
+    X.a[c] = *reinterpret_cast<const u32x4*>(xr + kk);
+    X.b[c] = *reinterpret_cast<const u32x4*>(xr + kk + 8);
+  }
+}
+
+// The lane's activation values as float: bf16 -> float, rotated first when
+// ROT (the 8 lanes of a 128-block together).
+template <int NCH, bool ROT>
+__device__ __forceinline__ void prep_x(const XRow<NCH>& X, float (&xv)[NCH][16], int lane) {
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      xv[c][2 * w] = bf16_lo(X.a[c][w]);
+      xv[c][2 * w + 1] = bf16_hi(X.a[c][w]);
+      xv[c][8 + 2 * w] = bf16_lo(X.b[c][w]);
+      xv[c][8 + 2 * w + 1] = bf16_hi(X.b[c][w]);
+    }
+    if constexpr (ROT) rotate16(xv[c], lane);
+  }
+}
+
+// gate_up (and act) of the wave's RPW row pairs for one token (its prepared
+// activation values xv), stored at sorted row r.
+template <int NCH, int RPW>
+__device__ __forceinline__ void gemv_row(const WaveRows<NCH, RPW>& R, const float (&xv)[NCH][16], int K, int N,
+                                         int i0, size_t r, float* __restrict__ gu, float* __restrict__ act,
+                                         int lane) {
+  const int I = N / 2;
+  float v[2 * RPW];
+#pragma unroll
+  for (int q = 0; q < 2 * RPW; ++q) v[q] = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    // a piece past K (a copy of the last one: finite) counts with weight 0
+    const bool inside = 16 * (lane + kWave * c) < K;
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      // the codes are loop-invariant over rows; an empty asm keeps their
+      // conversion here (hoisted, it would hold every code as a float)
+      u32x4 qg = R.cg[j][c], qu = R.cu[j][c];
+      asm volatile("" : "+v"(qg), "+v"(qu));
+      float pg0 = 0.0f, pg1 = 0.0f, pu0 = 0.0f, pu1 = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        pg0 = fmaf(sbyte<0>(qg[w]), xv[c][4 * w + 0], pg0);
+        pg1 = fmaf(sbyte<1>(qg[w]), xv[c][4 * w + 1], pg1);
+        pg0 = fmaf(sbyte<2>(qg[w]), xv[c][4 * w + 2], pg0);
+        pg1 = fmaf(sbyte<3>(qg[w]), xv[c][4 * w + 3], pg1);
+        pu0 = fmaf(sbyte<0>(qu[w]), xv[c][4 * w + 0], pu0);
+        pu1 = fmaf(sbyte<1>(qu[w]), xv[c][4 * w + 1], pu1);
+        pu0 = fmaf(sbyte<2>(qu[w]), xv[c][4 * w + 2], pu0);
+        pu1 = fmaf(sbyte<3>(qu[w]), xv[c][4 * w + 3], pu1);
+      }
+      v[2 * j] = fmaf(inside ? bf16_lo(R.sg[j][c]) : 0.0f, pg0 + pg1, v[2 * j]);
+      v[2 * j + 1] = fmaf(inside ? bf16_lo(R.su[j][c]) : 0.0f, pu0 + pu1, v[2 * j + 1]);
+    }
+  }
+  // v = (g0, u0, g1, u1, ...): fold halves over bits 5, 4 (and 3), then sum
+  // the lanes that share the kept index
+  fold_half<32>(v, lane);            // v[0 .. RPW) now hold the kept half
+  float w[RPW];
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) w[q] = v[q];
+  fold_half<16>(w, lane);            // w[0 .. RPW/2)
+  float s;
+  int up_bit;
+  if constexpr (RPW == 4) {
+    float z[2] = {w[0], w[1]};
+    fold_half<8>(z, lane);
+    s = z[0];
+    s += xor_lane<1>(s);
+    s += xor_lane<2>(s);
+    s += xor_lane<4>(s);
+    up_bit = 8;
+  } else {
+    s = w[0];
+    s += xor_lane<1>(s);
+    s += xor_lane<2>(s);
+    s += xor_lane<4>(s);
+    s += xor_lane<8>(s);
+    up_bit = 16;
+  }
+  // lane holds gate (up_bit clear) or up (up_bit set) of pair j
+  float other = (up_bit == 8) ? xor_lane<8>(s) : xor_lane<16>(s);
+  const int jmask = (up_bit == 8) ? 15 : 31;
+  if ((lane & jmask) == 0) {
+    const int j = (up_bit == 8) ? (lane >> 4) : (lane >> 5);
+    const float g = s, u = other;
+    if (gu) {
+      gu[r * N + i0 + j] = g;
+      gu[r * N + I + i0 + j] = u;
+    }
+    if (act) act[r * I + i0 + j] = gelu_tanh(g) * u;
+  }
+}
+
 template <int NCH, int RPW, bool ROT>
 __global__ void __launch_bounds__(kGemvThreads)
 k_gateup_i8h_gemv(const uint16_t* __restrict__ xin, int K, const int8_t* __restrict__ codes,
@@ -103,124 +274,105 @@ k_gateup_i8h_gemv(const uint16_t* __restrict__ xin, int K, const int8_t* __restr
   const int I = N / 2;
   const int i0 = (blockIdx.x * kGemvWaves + wave) * RPW;  // I % RPW == 0, so all RPW rows exist
   if (i0 >= I) return;
-  const int e = nth_nonempty_expert(expert_off, E, blockIdx.y, lane);
-  if (e < 0) return;
-  const int r0 = expert_off[e], r1 = expert_off[e + 1];
-  const int G = K / kGroup;
-
-  u32x4 cg[RPW][NCH], cu[RPW][NCH];
-  float sg[RPW][NCH], su[RPW][NCH];
-#pragma unroll
-  for (int j = 0; j < RPW; ++j) {
-    const int8_t* rowg = codes + ((size_t)e * N + i0 + j) * K;
-    const int8_t* rowu = codes + ((size_t)e * N + I + i0 + j) * K;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      int kk = 16 * (lane + kWave * c);
-      if (kk < K) {
-        cg[j][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowg + kk));
-        cu[j][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowu + kk));
-      } else {
-        cg[j][c] = u32x4{0u, 0u, 0u, 0u};
-        cu[j][c] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < RPW; ++j) {
-    const uint16_t* srg = scales + ((size_t)e * N + i0 + j) * G;
-    const uint16_t* sru = scales + ((size_t)e * N + I + i0 + j) * G;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      int kk = 16 * (lane + kWave * c);
-      int g = kk < K ? kk / kGroup : 0;
-      sg[j][c] = bf16_to_f32(srg[g]);
-      su[j][c] = bf16_to_f32(sru[g]);
-    }
-  }
-
+  int e, r0, r1;
+  if (!nth_nonempty_expert(expert_off, E, blockIdx.y, lane, e, r0, r1)) return;
+  // issue order: the first row's token (scalar load), scales and codes, then
+  // that row's activations; the next row's activations are fetched while the
+  // current row is being reduced
+  const int p0 = sorted_pairs[r0];
+  __builtin_amdgcn_sched_barrier(0);  // (the scheduler would otherwise wait for p0 before the code loads)
+  WaveRows<NCH, RPW> R;
+  load_rows(R, codes, scales, e, N, K, i0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  int t = p0 / k;
+  XRow<NCH> X;
+  load_x(X, xin + (size_t)t * K, K, lane);
   for (int r = r0; r < r1; ++r) {
-    const int t = sorted_pairs[r] / k;
-    const uint16_t* xr = xin + (size_t)t * K;
-    float v[2 * RPW];
-#pragma unroll
-    for (int q = 0; q < 2 * RPW; ++q) v[q] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      int kk = 16 * (lane + kWave * c);
-      u32x4 xa = {0u, 0u, 0u, 0u}, xb = {0u, 0u, 0u, 0u};
-      if (kk < K) {
-        xa = *reinterpret_cast<const u32x4*>(xr + kk);
-        xb = *reinterpret_cast<const u32x4*>(xr + kk + 8);
-      }
-      float xv[16];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        xv[2 * w] = bf16_lo(xa[w]);
-        xv[2 * w + 1] = bf16_hi(xa[w]);
-        xv[8 + 2 * w] = bf16_lo(xb[w]);
-        xv[8 + 2 * w + 1] = bf16_hi(xb[w]);
-      }
-      if constexpr (ROT) rotate16(xv, lane);
-#pragma unroll
-      for (int j = 0; j < RPW; ++j) {
-        // the codes are loop-invariant; an empty asm keeps their conversion
-        // inside the loop (hoisted, it would hold every code as a float)
-        u32x4 qg = cg[j][c], qu = cu[j][c];
-        asm volatile("" : "+v"(qg), "+v"(qu));
-        float pg0 = 0.0f, pg1 = 0.0f, pu0 = 0.0f, pu1 = 0.0f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          pg0 = fmaf(sbyte<0>(qg[w]), xv[4 * w + 0], pg0);
-          pg1 = fmaf(sbyte<1>(qg[w]), xv[4 * w + 1], pg1);
-          pg0 = fmaf(sbyte<2>(qg[w]), xv[4 * w + 2], pg0);
-          pg1 = fmaf(sbyte<3>(qg[w]), xv[4 * w + 3], pg1);
-          pu0 = fmaf(sbyte<0>(qu[w]), xv[4 * w + 0], pu0);
-          pu1 = fmaf(sbyte<1>(qu[w]), xv[4 * w + 1], pu1);
-          pu0 = fmaf(sbyte<2>(qu[w]), xv[4 * w + 2], pu0);
-          pu1 = fmaf(sbyte<3>(qu[w]), xv[4 * w + 3], pu1);
-        }
-        v[2 * j] = fmaf(sg[j][c], pg0 + pg1, v[2 * j]);
-        v[2 * j + 1] = fmaf(su[j][c], pu0 + pu1, v[2 * j + 1]);
+    float xv[NCH][16];
+    prep_x<NCH, ROT>(X, xv, lane);
+    if (r + 1 < r1) {
+      t = sorted_pairs[r + 1] / k;
+      load_x(X, xin + (size_t)t * K, K, lane);
+    }
+    gemv_row<NCH, RPW>(R, xv, K, N, i0, (size_t)r, gu, act, lane);
+  }
+}
+
+template <int NCH, int RPW, int VPL>
+__global__ void __launch_bounds__(kGemvThreads)
+k_route_gateup_decode(const float* __restrict__ logits, const uint16_t* __restrict__ x, int T, int K,
+                      const int8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int E, int N, int k,
+                      int32_t* __restrict__ ids_out, float* __restrict__ w_out, int32_t* __restrict__ expert_off,
+                      int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos,
+                      float* __restrict__ gu, float* __restrict__ act) {
+  __shared__ int s_ids[kWave];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int I = N / 2;
+  const bool writer = blockIdx.x == 0 && blockIdx.y == 0;  // stores the routing outputs
+  const int P = T * k;                                     // <= 64
+
+  // top-k of every token, a wave per token
+  for (int t = wave; t < T; t += kGemvWaves) {
+    int id;
+    float wt;
+    wave_topk<VPL>(logits + (size_t)t * E, E, k, lane, id, wt);
+    if (lane < k) {
+      s_ids[t * k + lane] = id;
+      if (writer) {
+        ids_out[t * k + lane] = id;
+        w_out[t * k + lane] = wt;
       }
     }
-    // v = (g0, u0, g1, u1, ...): fold halves over bits 5, 4 (and 3), then sum
-    // the lanes that share the kept index
-    fold_half<32>(v, lane);            // v[0 .. RPW) now hold the kept half
-    float w[RPW];
-#pragma unroll
-    for (int q = 0; q < RPW; ++q) w[q] = v[q];
-    fold_half<16>(w, lane);            // w[0 .. RPW/2)
-    float s;
-    int up_bit;
-    if constexpr (RPW == 4) {
-      float z[2] = {w[0], w[1]};
-      fold_half<8>(z, lane);
-      s = z[0];
-      s += xor_lane<1>(s);
-      s += xor_lane<2>(s);
-      s += xor_lane<4>(s);
-      up_bit = 8;
-    } else {
-      s = w[0];
-      s += xor_lane<1>(s);
-      s += xor_lane<2>(s);
-      s += xor_lane<4>(s);
-      s += xor_lane<8>(s);
-      up_bit = 16;
+  }
+  __syncthreads();
+
+  // group the pairs by expert (each wave on its own, same result everywhere)
+  const bool valid = lane < P;
+  const int ep = valid ? s_ids[lane] : 0;
+  const PairGroup pg = wave_group_by_expert(valid, ep, bits_for(E));
+  const int below = __popcll(pg.lt);                     // first sorted row of the pair's expert
+  const int rank = __popcll(pg.eq & lanes_below(lane));  // stable rank inside it
+  const uint64_t first = __ballot(valid && rank == 0);   // one lane per non-empty expert
+  const int slot = __popcll(pg.lt & first);              // the expert's place among the non-empty ones
+  if (writer && wave == 0 && valid) {
+    sorted_pairs[below + rank] = lane;
+    pair_pos[lane] = below + rank;
+  }
+  if (writer) {
+    // expert_off[e] = number of pairs routed to experts below e
+    for (int e = threadIdx.x; e <= E; e += kGemvThreads) {
+      int c = 0;
+      for (int q = 0; q < P; ++q) c += s_ids[q] < e;
+      expert_off[e] = c;
     }
-    // lane holds gate (up_bit clear) or up (up_bit set) of pair j
-    float other = (up_bit == 8) ? xor_lane<8>(s) : xor_lane<16>(s);
-    const int jmask = (up_bit == 8) ? 15 : 31;
-    if ((lane & jmask) == 0) {
-      const int j = (up_bit == 8) ? (lane >> 4) : (lane >> 5);
-      const float g = s, u = other;
-      if (gu) {
-        gu[(size_t)r * N + i0 + j] = g;
-        gu[(size_t)r * N + I + i0 + j] = u;
-      }
-      if (act) act[(size_t)r * I + i0 + j] = gelu_tanh(g) * u;
-    }
+  }
+  const uint64_t mine = __ballot(valid && rank == 0 && slot == (int)blockIdx.y);
+  const int i0 = (blockIdx.x * kGemvWaves + wave) * RPW;
+  if (mine == 0 || i0 >= I) return;
+  const int L = __ffsll((unsigned long long)mine) - 1;
+  const int e = __builtin_amdgcn_readlane(ep, L);
+  const int r0 = __builtin_amdgcn_readlane(below, L);
+  uint64_t rows = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(pg.eq >> 32), L) << 32) |
+                  (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pg.eq, L);
+
+  // the first row's activations go out before the codes, so that their
+  // rotation runs while the code stream is still arriving
+  int p = __ffsll((unsigned long long)rows) - 1;  // pairs of the expert in increasing order
+  rows &= rows - 1;
+  XRow<NCH> X;
+  load_x(X, x + (size_t)(p / k) * K, K, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  WaveRows<NCH, RPW> R;
+  load_rows(R, codes, scales, e, N, K, i0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int r = r0; p >= 0; ++r) {
+    float xv[NCH][16];
+    prep_x<NCH, true>(X, xv, lane);
+    p = rows ? __ffsll((unsigned long long)rows) - 1 : -1;
+    rows &= rows - 1;
+    if (p >= 0) load_x(X, x + (size_t)(p / k) * K, K, lane);
+    gemv_row<NCH, RPW>(R, xv, K, N, i0, (size_t)r, gu, act, lane);
   }
 }
 
@@ -258,6 +410,40 @@ hipError_t launch_gateup_i8h_gemv_rot(const uint16_t* x, int T, int K, const int
                                       const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
                                       const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st) {
   return launch_gemv<true>(x, T, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu, act, st);
+}
+
+template <int NCH, int RPW>
+static void launch_decode(dim3 grid, int vpl, const float* logits, const uint16_t* x, int T, int K,
+                          const int8_t* codes, const uint16_t* scales, int E, int N, int k, int32_t* ids, float* w,
+                          int32_t* expert_off, int32_t* sorted_pairs, int32_t* pair_pos, float* gu, float* act,
+                          hipStream_t st) {
+#define I8H_DECODE_ARGS logits, x, T, K, codes, scales, E, N, k, ids, w, expert_off, sorted_pairs, pair_pos, gu, act
+  if (vpl <= 1) k_route_gateup_decode<NCH, RPW, 1><<<grid, kGemvThreads, 0, st>>>(I8H_DECODE_ARGS);
+  else if (vpl <= 2) k_route_gateup_decode<NCH, RPW, 2><<<grid, kGemvThreads, 0, st>>>(I8H_DECODE_ARGS);
+  else k_route_gateup_decode<NCH, RPW, 4><<<grid, kGemvThreads, 0, st>>>(I8H_DECODE_ARGS);
+#undef I8H_DECODE_ARGS
+}
+
+hipError_t launch_route_gateup_decode(const float* logits, const uint16_t* x, int T, int K, const int8_t* codes,
+                                      const uint16_t* scales, int E, int N, int k, int32_t* ids, float* w,
+                                      int32_t* expert_off, int32_t* sorted_pairs, int32_t* pair_pos, float* gu,
+                                      float* act, hipStream_t st) {
+  int P = T * k;
+  int slots = P < E ? P : E;
+  int I = N / 2;
+  int nch = cdiv(K, 16 * kWave);
+  int vpl = cdiv(E, kWave);
+  if (nch <= 1) {
+    launch_decode<1, 4>(dim3(cdiv(I, kGemvWaves * 4), slots), vpl, logits, x, T, K, codes, scales, E, N, k, ids, w,
+                        expert_off, sorted_pairs, pair_pos, gu, act, st);
+  } else if (nch <= 2) {
+    launch_decode<2, 4>(dim3(cdiv(I, kGemvWaves * 4), slots), vpl, logits, x, T, K, codes, scales, E, N, k, ids, w,
+                        expert_off, sorted_pairs, pair_pos, gu, act, st);
+  } else {
+    launch_decode<4, 2>(dim3(cdiv(I, kGemvWaves * 2), slots), vpl, logits, x, T, K, codes, scales, E, N, k, ids, w,
+                        expert_off, sorted_pairs, pair_pos, gu, act, st);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace i8h

@@ -29,6 +29,11 @@ hipError_t launch_gateup_i8h_gemv_rot(const uint16_t* x, int T, int K, const int
                                       const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
                                       const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st);
 
+hipError_t launch_route_gateup_decode(const float* logits, const uint16_t* x, int T, int K, const int8_t* codes,
+                                      const uint16_t* scales, int E, int N, int k, int32_t* ids, float* w,
+                                      int32_t* expert_off, int32_t* sorted_pairs, int32_t* pair_pos, float* gu,
+                                      float* act, hipStream_t st);
+
 hipError_t launch_fp8_act_quant(const uint16_t* x, int T, int K, uint8_t* qx, float* sx, uint16_t* xq,
                                 hipStream_t st);
 hipError_t launch_gateup_fp8(const uint16_t* xq, const float* sx, int T, int K, const uint8_t* codes,

@@ -17,67 +17,12 @@
 
 #include "common.hpp"
 #include "launch.hpp"
-#include "xlane.hpp"
+#include "topk.hpp"
 
 namespace i8h {
 
 constexpr int kChunkPairs = 256;   // pairs per histogram/scatter block
 constexpr int kRouteThreads = 256;
-
-// Keep the better of this lane's and its xor-M partner's candidate.
-template <int M>
-__device__ __forceinline__ void best_step(float& bv, int& bi) {
-  float ov = xor_lane<M>(bv);
-  int oi = xor_lane_i<M>(bi);
-  if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-}
-
-// --- top-k of one token, by one wave ------------------------------------
-// Lane l holds logits e = l + 64 v. Each round takes the wave-wide best
-// (largest value, then lowest index), then retires it.
-template <int VPL>
-__device__ __forceinline__ void topk_one_token(const float* __restrict__ row, int E, int k, int lane,
-                                               int32_t* __restrict__ ids_out, float* __restrict__ w_out,
-                                               int* lds_ids /* may be null */) {
-  float v[VPL];
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    int e = lane + kWave * i;
-    v[i] = e < E ? row[e] : 0.0f;
-  }
-  uint32_t retired = 0;  // bit i: v[i] already taken
-  int my_id = 0;
-  float my_logit = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    // best of this lane: indices grow with i, so a strict '>' keeps the lowest tie
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      int e = lane + kWave * i;
-      bool open = e < E && !((retired >> i) & 1u);
-      if (open && (bi == 0x7fffffff || v[i] > bv)) { bv = v[i]; bi = e; }
-    }
-    // wave-wide best: larger value first, then lower index (a total order,
-    // so every lane ends with the same winner)
-    best_step<1>(bv, bi);
-    best_step<2>(bv, bi);
-    best_step<4>(bv, bi);
-    best_step<8>(bv, bi);
-    best_step<16>(bv, bi);
-    best_step<32>(bv, bi);
-    if ((bi % kWave) == lane) retired |= 1u << (bi / kWave);
-    if (lane == j) { my_id = bi; my_logit = bv; }
-  }
-  float l0 = __shfl(my_logit, 0, kWave);
-  float ex = lane < k ? expf(my_logit - l0) : 0.0f;
-  float sum = wave_sum(ex);
-  if (lane < k) {
-    ids_out[lane] = my_id;
-    w_out[lane] = ex / sum;
-    if (lds_ids) lds_ids[lane] = my_id;
-  }
-}
 
 template <int VPL>
 __global__ void __launch_bounds__(kRouteThreads)
@@ -86,7 +31,13 @@ k_route_topk(const float* __restrict__ logits, int T, int E, int k,
   int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   int t = blockIdx.x * (kRouteThreads / kWave) + wave;
   if (t >= T) return;
-  topk_one_token<VPL>(logits + (size_t)t * E, E, k, lane, ids + (size_t)t * k, w + (size_t)t * k, nullptr);
+  int id;
+  float wt;
+  wave_topk<VPL>(logits + (size_t)t * E, E, k, lane, id, wt);
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = id;
+    w[(size_t)t * k + lane] = wt;
+  }
 }
 
 // --- histogram of one chunk of pairs -------------------------------------
@@ -156,11 +107,6 @@ __device__ __forceinline__ int block_stable_rank(bool valid, int e, int E, int n
   return prefix + rank_w;
 }
 
-__device__ __forceinline__ int bits_for(int E) {
-  int nb = 0;
-  while ((1 << nb) < E) ++nb;
-  return nb;
-}
 
 // --- totals, scan and stable scatter of one chunk ------------------------
 __global__ void __launch_bounds__(kRouteThreads)
@@ -216,9 +162,16 @@ k_route_small(const float* __restrict__ logits, int T, int E, int k,
   int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
   for (int i = threadIdx.x; i < 4 * E; i += blockDim.x) wcount[i] = 0;
-  if (wave < T)
-    topk_one_token<VPL>(logits + (size_t)wave * E, E, k, lane, ids + (size_t)wave * k, w + (size_t)wave * k,
-                        lds_ids + wave * k);
+  if (wave < T) {
+    int id;
+    float wt;
+    wave_topk<VPL>(logits + (size_t)wave * E, E, k, lane, id, wt);
+    if (lane < k) {
+      ids[(size_t)wave * k + lane] = id;
+      w[(size_t)wave * k + lane] = wt;
+      lds_ids[wave * k + lane] = id;
+    }
+  }
   __syncthreads();
   int P = T * k;
   int p = threadIdx.x;

@@ -1,0 +1,103 @@
+// Wave-level routing pieces shared by the router kernels and the fused decode
+// kernel.
+//
+// Rule (the int8 card's model table, row "Weights", describes routed experts
+// picked by a router and prints no rule): token t takes the k experts of
+// largest logit, ties to the lower expert index, weights = softmax over the k
+// chosen logits. Pairs p = t*k + j are grouped by expert with increasing p
+// inside each expert.
+#pragma once
+
+#include "common.hpp"
+#include "xlane.hpp"
+
+namespace i8h {
+
+// Wave-wide float maximum (every lane gets it).
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, xor_lane<32>(v));
+  v = fmaxf(v, xor_lane<16>(v));
+  v = fmaxf(v, xor_lane<8>(v));
+  v = fmaxf(v, xor_lane<4>(v));
+  v = fmaxf(v, xor_lane<2>(v));
+  v = fmaxf(v, xor_lane<1>(v));
+  return v;
+}
+
+// Top-k of one token by one wave. Lane l holds logits e = l + 64 i. Each
+// round takes the largest open value (a wave maximum) and, among the open
+// entries equal to it, the lowest expert index (ballots in index order), then
+// retires that entry: the order "larger value first, then lower index".
+// Lane j < k returns the j-th choice and its softmax weight; other lanes
+// return id -1.
+template <int VPL>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int lane, int& id,
+                                          float& weight) {
+  float v[VPL];
+  uint32_t open = 0;  // bit i: v[i] is a logit not yet taken
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = lane + kWave * i;
+    v[i] = e < E ? row[e] : -INFINITY;
+    if (e < E) open |= 1u << i;
+  }
+  int my_id = -1;
+  float my_logit = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if ((open >> i) & 1u) m = fmaxf(m, v[i]);
+    m = wave_max(m);
+    int best = -1;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const uint64_t b = __ballot(((open >> i) & 1u) && v[i] == m);
+      if (best < 0 && b != 0) best = kWave * i + __ffsll((unsigned long long)b) - 1;
+    }
+    if ((best % kWave) == lane) open &= ~(1u << (best / kWave));
+    if (lane == j) { my_id = best; my_logit = m; }
+  }
+  const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_logit), 0));
+  float ex = lane < k ? expf(my_logit - l0) : 0.0f;
+  float sum = wave_sum(ex);
+  id = my_id;
+  weight = lane < k ? ex / sum : 0.0f;
+}
+
+// Grouping of up to 64 pairs by expert inside one wave: lane p holds pair p
+// (valid) routed to expert e (0 <= e < 2^nbits). Radix over the bits of e,
+// most significant first, with one ballot per bit:
+//   lt = lanes whose expert is smaller than e, eq = lanes with expert e.
+// Then |lt| is the expert's first sorted row and |eq below p| the pair's rank
+// inside its expert (the stable order).
+struct PairGroup {
+  uint64_t lt, eq;
+};
+__device__ __forceinline__ PairGroup wave_group_by_expert(bool valid, int e, int nbits) {
+  PairGroup g;
+  g.lt = 0;
+  g.eq = __ballot(valid);
+  for (int b = nbits - 1; b >= 0; --b) {
+    const bool bit = valid && ((e >> b) & 1);
+    const uint64_t B = __ballot(bit);
+    if (bit) {
+      g.lt |= g.eq & ~B;
+      g.eq &= B;
+    } else {
+      g.eq &= ~B;
+    }
+  }
+  if (!valid) g.eq = 0;
+  return g;
+}
+
+__device__ __forceinline__ uint64_t lanes_below(int lane) { return lane == 0 ? 0ull : (~0ull >> (kWave - lane)); }
+
+__device__ __forceinline__ int bits_for(int E) {
+  int nb = 0;
+  while ((1 << nb) < E) ++nb;
+  return nb;
+}
+
+}  // namespace i8h

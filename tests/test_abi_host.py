@@ -33,7 +33,7 @@ def L():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -132,3 +132,21 @@ def test_fp8_validation(L):
     assert q(A, 4, 100, A, A, None) == EINVAL
     assert q(ODD, 4, 128, A, A, None) == EINVAL
     assert q(A, 0, 128, A, A, None) == OK
+
+
+def dec(L, lg=A, x=A, T=1, K=2048, codes=A, scales=A, E=128, N=1536, k=8, gu=A, act=A, ids=A):
+    return L.moe_route_gateup_i8h_decode(lg, x, T, K, codes, scales, E, N, k, ids, A, A, A, A, gu, act, None)
+
+
+def test_decode_validation(L):
+    assert dec(L, K=100) == EINVAL
+    assert dec(L, N=96) == EINVAL                    # N % 64
+    assert dec(L, T=9) == EUNSUP                     # 72 pairs > 64
+    assert dec(L, E=257, k=8) == EUNSUP              # more than 4 logits per lane
+    assert dec(L, K=8192) == EUNSUP
+    assert dec(L, T=0) == OK
+    assert dec(L, lg=None) == EINVAL
+    assert dec(L, ids=None) == EINVAL                # routing outputs are required
+    assert dec(L, gu=None, act=None) == EINVAL       # nothing to compute
+    assert dec(L, x=ODD) == EINVAL
+    assert dec(L, lg=ODD) == EINVAL

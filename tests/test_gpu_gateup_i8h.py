@@ -17,7 +17,8 @@ import torch
 import int8_hadamard_domain_amd as i8h
 import synth
 from oracle import gateup, hadamard, numfmt, quant, router
-from tests.gpu_util import assert_close, bf16_bits_of, bf16_cuda, fwht_tie_window, near_tie_mask
+from tests.gpu_util import (assert_close, bf16_bits_of, bf16_cuda, check_with_rotation_slack, fwht_tie_window,
+                             near_tie_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -247,31 +248,7 @@ def test_fused_rotation(gpu_available, name, T):
         bf16_cuda(xb), torch.from_numpy(codes).cuda(), bf16_cuda(sbits), L.topk,
         torch.from_numpy(r["expert_off"]).cuda(), torch.from_numpy(r["sorted_pairs"]).cuda())
     torch.cuda.synchronize()
-    _check_with_rotation_slack(L, x, codes, sbits, r, gu, act)
-
-
-def _check_with_rotation_slack(L, x, codes, sbits, r, gu, act):
-    exact = hadamard.rotate_blocks(x)
-    x_rot = numfmt.bf16_round(exact)
-    scales = numfmt.bf16_from_bits(sbits)
-    ref = gateup.gateup_i8h(x_rot, codes, scales, r["expert_off"], r["sorted_pairs"], L.topk)
-    tie = near_tie_mask(exact, fwht_tie_window(x))
-    ulp = np.ldexp(1.0, np.frexp(np.abs(x_rot) + 1e-300)[1] - 8)
-    slack_x = np.where(tie, ulp, 0.0)
-    off, sp = r["expert_off"], r["sorted_pairs"]
-    what = quant.dequantize_i8h(codes, scales)
-    slack = np.zeros_like(ref)
-    for row in range(ref.shape[0]):
-        e = np.searchsorted(off, row, side="right") - 1
-        slack[row] = np.abs(what[e]) @ slack_x[sp[row] // L.topk]
-    g = gu.cpu().numpy().astype(np.float64)
-    assert np.all(np.abs(g - ref) <= 1e-4 * np.abs(ref) + 1e-5 + slack)
-    I = L.N // 2
-    ref_act = gateup.epilogue(ref)
-    dg, du = slack[:, :I], slack[:, I:]
-    act_slack = 1.13 * dg * (np.abs(ref[:, I:]) + du) + np.abs(gateup.gelu_tanh(ref[:, :I])) * du
-    a = act.cpu().numpy().astype(np.float64)
-    assert np.all(np.abs(a - ref_act) <= 1e-4 * np.abs(ref_act) + 1e-5 + act_slack)
+    check_with_rotation_slack(x, codes, sbits, r, L.topk, gu, act)
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode"])
