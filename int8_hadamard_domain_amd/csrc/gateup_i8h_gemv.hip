@@ -34,7 +34,9 @@
 // token), groups the pairs by expert with ballots, picks the expert of its
 // slot and goes on as above; block (0, 0) also stores the routing outputs.
 // One launch then covers route -> rotate -> gate_up, and no block waits for
-// another kernel's results.
+// another kernel's results. The two waves of a block split the rotation of a
+// token row and share it through LDS; with a single token the row is fetched
+// before the routing, and the rotation runs after the code loads are issued.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -43,7 +45,7 @@
 
 namespace i8h {
 
-constexpr int kGemvThreads = 256;
+constexpr int kGemvThreads = 128;  // two waves: the decode grid spreads evenly over the CUs
 constexpr int kGemvWaves = kGemvThreads / kWave;
 constexpr int kScanChunks = 4;  // expert_off entries per lane and round trip (E <= 256 in one)
 
@@ -147,13 +149,15 @@ __device__ __forceinline__ void load_rows(WaveRows<NCH, RPW>& R, const int8_t* _
       R.su[j][c] = sru[g];
     }
   }
+  // in the order the dot products consume them (piece-major): loads complete
+  // in issue order, so the first pieces can be used while the rest arrive
 #pragma unroll
-  for (int j = 0; j < RPW; ++j) {
-    const int8_t* rowg = codes + ((size_t)e * N + i0 + j) * K;
-    const int8_t* rowu = codes + ((size_t)e * N + I + i0 + j) * K;
+  for (int c = 0; c < NCH; ++c) {
+    const int kk = min(16 * (lane + kWave * c), K - 16);  // pieces past K re-read the last one
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int kk = min(16 * (lane + kWave * c), K - 16);  // pieces past K re-read the last one
+    for (int j = 0; j < RPW; ++j) {
+      const int8_t* rowg = codes + ((size_t)e * N + i0 + j) * K;
+      const int8_t* rowu = codes + ((size_t)e * N + I + i0 + j) * K;
       R.cg[j][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowg + kk));
       R.cu[j][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowu + kk));
     }
@@ -298,6 +302,66 @@ k_gateup_i8h_gemv(const uint16_t* __restrict__ xin, int K, const int8_t* __restr
   }
 }
 
+// The rotation of one token row is shared by the two waves of a block: wave
+// w rotates the pieces c = w, w + 2, .. (64 lanes x 16 values each) and
+// leaves them as bf16 in LDS, where both waves read the whole row.
+template <int NCH>
+struct RotShare {
+  static constexpr int kN = (NCH + 1) / 2;
+  XRow<kN> X;
+
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ xr, int K, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int kk = min(16 * (lane + kWave * (wave + 2 * i)), K - 16);  // past K: a copy (weight 0 later)
+      X.a[i] = *reinterpret_cast<const u32x4*>(xr + kk);
+      X.b[i] = *reinterpret_cast<const u32x4*>(xr + kk + 8);
+    }
+  }
+
+  __device__ __forceinline__ void rotate_to(uint16_t* s_xr, int wave, int lane) const {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int c = wave + 2 * i;
+      if (c >= NCH) break;  // uniform in the wave
+      float xv[16];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        xv[2 * w] = bf16_lo(X.a[i][w]);
+        xv[2 * w + 1] = bf16_hi(X.a[i][w]);
+        xv[8 + 2 * w] = bf16_lo(X.b[i][w]);
+        xv[8 + 2 * w + 1] = bf16_hi(X.b[i][w]);
+      }
+      rotate16(xv, lane);
+      u32x4 lo, hi;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        lo[w] = pack_bf16x2(xv[2 * w], xv[2 * w + 1]);       // exact: already bf16 values
+        hi[w] = pack_bf16x2(xv[8 + 2 * w], xv[8 + 2 * w + 1]);
+      }
+      u32x4* dst = reinterpret_cast<u32x4*>(s_xr + 16 * (lane + kWave * c));
+      dst[0] = lo;
+      dst[1] = hi;
+    }
+  }
+};
+
+template <int NCH>
+__device__ __forceinline__ void read_rotated(const uint16_t* s_xr, float (&xv)[NCH][16], int lane) {
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(s_xr + 16 * (lane + kWave * c));
+    const u32x4 a = src[0], b = src[1];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      xv[c][2 * w] = bf16_lo(a[w]);
+      xv[c][2 * w + 1] = bf16_hi(a[w]);
+      xv[c][8 + 2 * w] = bf16_lo(b[w]);
+      xv[c][8 + 2 * w + 1] = bf16_hi(b[w]);
+    }
+  }
+}
+
 template <int NCH, int RPW, int VPL>
 __global__ void __launch_bounds__(kGemvThreads)
 k_route_gateup_decode(const float* __restrict__ logits, const uint16_t* __restrict__ x, int T, int K,
@@ -305,18 +369,29 @@ k_route_gateup_decode(const float* __restrict__ logits, const uint16_t* __restri
                       int32_t* __restrict__ ids_out, float* __restrict__ w_out, int32_t* __restrict__ expert_off,
                       int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos,
                       float* __restrict__ gu, float* __restrict__ act) {
+  static_assert(kGemvWaves == 2, "the rotation is shared by two waves");
   __shared__ int s_ids[kWave];
+  __shared__ __attribute__((aligned(16))) uint16_t s_xr[NCH * 16 * kWave];  // rotated row, bf16
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int I = N / 2;
   const bool writer = blockIdx.x == 0 && blockIdx.y == 0;  // stores the routing outputs
   const int P = T * k;                                     // <= 64
 
+  // the first token's logits go out first; with a single token its
+  // activations are needed whatever the routing, so they follow at once and
+  // are in registers long before the code stream
+  float lv[VPL];
+  if (wave < T) load_logits<VPL>(logits + (size_t)wave * E, E, lane, lv);
+  RotShare<NCH> share;
+  if (T == 1) share.load(x, K, wave, lane);
+
   // top-k of every token, a wave per token
   for (int t = wave; t < T; t += kGemvWaves) {
     int id;
     float wt;
-    wave_topk<VPL>(logits + (size_t)t * E, E, k, lane, id, wt);
+    if (t != wave) load_logits<VPL>(logits + (size_t)t * E, E, lane, lv);
+    wave_topk<VPL>(lv, E, k, lane, id, wt);
     if (lane < k) {
       s_ids[t * k + lane] = id;
       if (writer) {
@@ -335,43 +410,52 @@ k_route_gateup_decode(const float* __restrict__ logits, const uint16_t* __restri
   const int rank = __popcll(pg.eq & lanes_below(lane));  // stable rank inside it
   const uint64_t first = __ballot(valid && rank == 0);   // one lane per non-empty expert
   const int slot = __popcll(pg.lt & first);              // the expert's place among the non-empty ones
-  if (writer && wave == 0 && valid) {
-    sorted_pairs[below + rank] = lane;
-    pair_pos[lane] = below + rank;
-  }
-  if (writer) {
+  // the routing outputs: stored by block (0, 0) after its own code loads
+  // are on their way (below), or here if it has no rows to work on
+  auto store_routing = [&]() {
+    if (wave == 0 && valid) {
+      sorted_pairs[below + rank] = lane;
+      pair_pos[lane] = below + rank;
+    }
     // expert_off[e] = number of pairs routed to experts below e
     for (int e = threadIdx.x; e <= E; e += kGemvThreads) {
       int c = 0;
       for (int q = 0; q < P; ++q) c += s_ids[q] < e;
       expert_off[e] = c;
     }
-  }
+  };
+  // both waves of a block see the same slot and (I % 8 == 0) the same i0 range,
+  // so they leave together and meet at the barriers below
   const uint64_t mine = __ballot(valid && rank == 0 && slot == (int)blockIdx.y);
   const int i0 = (blockIdx.x * kGemvWaves + wave) * RPW;
-  if (mine == 0 || i0 >= I) return;
+  if (mine == 0 || i0 >= I) {
+    if (writer) store_routing();
+    return;
+  }
   const int L = __ffsll((unsigned long long)mine) - 1;
   const int e = __builtin_amdgcn_readlane(ep, L);
   const int r0 = __builtin_amdgcn_readlane(below, L);
   uint64_t rows = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(pg.eq >> 32), L) << 32) |
                   (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pg.eq, L);
 
-  // the first row's activations go out before the codes, so that their
-  // rotation runs while the code stream is still arriving
   int p = __ffsll((unsigned long long)rows) - 1;  // pairs of the expert in increasing order
   rows &= rows - 1;
-  XRow<NCH> X;
-  load_x(X, x + (size_t)(p / k) * K, K, lane);
+  if (T != 1) share.load(x + (size_t)(p / k) * K, K, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
   WaveRows<NCH, RPW> R;
   load_rows(R, codes, scales, e, N, K, i0, lane);
   __builtin_amdgcn_sched_barrier(0);
+  if (writer) store_routing();
   for (int r = r0; p >= 0; ++r) {
+    if (r != r0) __syncthreads();        // the previous row is read by both waves
+    share.rotate_to(s_xr, wave, lane);   // runs while the codes arrive
+    __syncthreads();
     float xv[NCH][16];
-    prep_x<NCH, true>(X, xv, lane);
+    read_rotated<NCH>(s_xr, xv, lane);
+    __builtin_amdgcn_sched_barrier(0);
     p = rows ? __ffsll((unsigned long long)rows) - 1 : -1;
     rows &= rows - 1;
-    if (p >= 0) load_x(X, x + (size_t)(p / k) * K, K, lane);
+    if (p >= 0) share.load(x + (size_t)(p / k) * K, K, wave, lane);
     gemv_row<NCH, RPW>(R, xv, K, N, i0, (size_t)r, gu, act, lane);
   }
 }
@@ -389,8 +473,8 @@ static hipError_t launch_gemv(const uint16_t* x, int T, int K, const int8_t* cod
     k_gateup_i8h_gemv<1, 4, ROT><<<grid, kGemvThreads, 0, st>>>(x, K, codes, scales, E, N, k, expert_off,
                                                                 sorted_pairs, gu, act);
   } else if (nch <= 2) {
-    dim3 grid(cdiv(I, kGemvWaves * 4), slots);
-    k_gateup_i8h_gemv<2, 4, ROT><<<grid, kGemvThreads, 0, st>>>(x, K, codes, scales, E, N, k, expert_off,
+    dim3 grid(cdiv(I, kGemvWaves * 2), slots);
+    k_gateup_i8h_gemv<2, 2, ROT><<<grid, kGemvThreads, 0, st>>>(x, K, codes, scales, E, N, k, expert_off,
                                                                 sorted_pairs, gu, act);
   } else {
     dim3 grid(cdiv(I, kGemvWaves * 2), slots);
@@ -437,7 +521,7 @@ hipError_t launch_route_gateup_decode(const float* logits, const uint16_t* x, in
     launch_decode<1, 4>(dim3(cdiv(I, kGemvWaves * 4), slots), vpl, logits, x, T, K, codes, scales, E, N, k, ids, w,
                         expert_off, sorted_pairs, pair_pos, gu, act, st);
   } else if (nch <= 2) {
-    launch_decode<2, 4>(dim3(cdiv(I, kGemvWaves * 4), slots), vpl, logits, x, T, K, codes, scales, E, N, k, ids, w,
+    launch_decode<2, 2>(dim3(cdiv(I, kGemvWaves * 2), slots), vpl, logits, x, T, K, codes, scales, E, N, k, ids, w,
                         expert_off, sorted_pairs, pair_pos, gu, act, st);
   } else {
     launch_decode<4, 2>(dim3(cdiv(I, kGemvWaves * 2), slots), vpl, logits, x, T, K, codes, scales, E, N, k, ids, w,

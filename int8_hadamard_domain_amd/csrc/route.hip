@@ -33,7 +33,9 @@ k_route_topk(const float* __restrict__ logits, int T, int E, int k,
   if (t >= T) return;
   int id;
   float wt;
-  wave_topk<VPL>(logits + (size_t)t * E, E, k, lane, id, wt);
+  float v[VPL];
+  load_logits<VPL>(logits + (size_t)t * E, E, lane, v);
+  wave_topk<VPL>(v, E, k, lane, id, wt);
   if (lane < k) {
     ids[(size_t)t * k + lane] = id;
     w[(size_t)t * k + lane] = wt;
@@ -165,7 +167,9 @@ k_route_small(const float* __restrict__ logits, int T, int E, int k,
   if (wave < T) {
     int id;
     float wt;
-    wave_topk<VPL>(logits + (size_t)wave * E, E, k, lane, id, wt);
+    float v[VPL];
+    load_logits<VPL>(logits + (size_t)wave * E, E, lane, v);
+    wave_topk<VPL>(v, E, k, lane, id, wt);
     if (lane < k) {
       ids[(size_t)wave * k + lane] = id;
       w[(size_t)wave * k + lane] = wt;

@@ -13,14 +13,16 @@
 
 namespace i8h {
 
-// Wave-wide float maximum (every lane gets it).
+// Wave-wide float maximum (every lane gets it). A maximum needs no exact
+// partner pattern: after the quad steps, rotations by 4 and 8 inside each
+// 16-lane row reach all four quads, then the row and half swaps.
 __device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, xor_lane<32>(v));
-  v = fmaxf(v, xor_lane<16>(v));
-  v = fmaxf(v, xor_lane<8>(v));
-  v = fmaxf(v, xor_lane<4>(v));
-  v = fmaxf(v, xor_lane<2>(v));
   v = fmaxf(v, xor_lane<1>(v));
+  v = fmaxf(v, xor_lane<2>(v));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
+  v = fmaxf(v, xor_lane<8>(v));
+  v = fmaxf(v, xor_lane<16>(v));
+  v = fmaxf(v, xor_lane<32>(v));
   return v;
 }
 
@@ -31,16 +33,20 @@ __device__ __forceinline__ float wave_max(float v) {
 // Lane j < k returns the j-th choice and its softmax weight; other lanes
 // return id -1.
 template <int VPL>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int lane, int& id,
-                                          float& weight) {
-  float v[VPL];
-  uint32_t open = 0;  // bit i: v[i] is a logit not yet taken
+__device__ __forceinline__ void load_logits(const float* __restrict__ row, int E, int lane, float (&v)[VPL]) {
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + kWave * i;
     v[i] = e < E ? row[e] : -INFINITY;
-    if (e < E) open |= 1u << i;
   }
+}
+
+template <int VPL>
+__device__ __forceinline__ void wave_topk(const float (&v)[VPL], int E, int k, int lane, int& id, float& weight) {
+  uint32_t open = 0;  // bit i: v[i] is a logit not yet taken
+#pragma unroll
+  for (int i = 0; i < VPL; ++i)
+    if (lane + kWave * i < E) open |= 1u << i;
   int my_id = -1;
   float my_logit = 0.0f;
   for (int j = 0; j < k; ++j) {
