@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes 4 times (the reference kernel "
+                         "whose FETCH_SIZE / WRITE_SIZE counters scale the HBM traffic figures)")
     ap.add_argument("--two-launch", action="store_true",
                     help="decode: time moe_route_permute + moe_gateup_i8h_grouped_fused instead of the "
                          "one-launch moe_route_gateup_i8h_decode")
@@ -72,6 +75,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_probe > 0:
+        a = torch.ones(args.copy_probe, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(4):
+            b.copy_(a)
+        torch.cuda.synchronize(dev)
+        print(json.dumps({"copy_probe_bytes": args.copy_probe, "copies": 4}))
+        return
     i8h.lib()
 
     name = args.workload
@@ -215,15 +226,17 @@ def main():
     achieved = alg_bytes / (kern_us * 1e-6) / 1e9
     flops = 2.0 * L.P * L.N * L.K
     if one_launch:
-        kernel_name = "k_route_gateup_decode (routing + rotation + gate_up)"
+        kernel_name, key = "k_route_gateup_decode (routing + rotation + gate_up)", "route_gateup_decode"
     elif fp8:
-        kernel_name = "k_gateup_gemm<E4M3> (+ k_fp8_act_quant)"
+        kernel_name, key = "k_gateup_gemm<E4M3> (+ k_fp8_act_quant)", "gemm_e4m3"
     elif args.path == "gemv" or (args.path == "auto" and L.T <= 8):
         kernel_name = "k_gateup_i8h_gemv" + ("<rotation fused>" if fused else "")
+        key = "gemv_rot" if fused else "gemv"
     else:
-        kernel_name = "k_gateup_gemm<I8>"
+        kernel_name, key = "k_gateup_gemm<I8>", "gemm_i8"
+    traffic = measured_traffic(key, name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": kernel_name,
                 "kernel_us": round(kern_us, 3), "alg_bytes_per_launch": int(alg_bytes),
                 "mfma_tflops": round(flops / (kern_us * 1e-6) / 1e12, 2)}
@@ -258,6 +271,38 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+# source files of each timed kernel: a traffic figure holds only for the sources it was measured on
+KERNEL_SOURCES = {
+    "route_gateup_decode": ["gateup_i8h_gemv.hip", "topk.hpp", "xlane.hpp", "common.hpp", "launch.hpp"],
+    "gemv": ["gateup_i8h_gemv.hip", "topk.hpp", "xlane.hpp", "common.hpp", "launch.hpp"],
+    "gemv_rot": ["gateup_i8h_gemv.hip", "topk.hpp", "xlane.hpp", "common.hpp", "launch.hpp"],
+    "gemm_i8": ["gateup_gemm.hip", "common.hpp", "launch.hpp"],
+    "gemm_e4m3": ["gateup_gemm.hip", "gateup_fp8.hip", "xlane.hpp", "common.hpp", "launch.hpp"],
+}
+
+
+def measured_traffic(key, workload):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled) from profiles/hbm_traffic.txt, or None
+    when there is no line for this kernel and workload or its sources changed since."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    csrc = os.path.join(here, "int8_hadamard_domain_amd", "csrc")
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[key]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    sha = h.hexdigest()[:16]
+    try:
+        with open(os.path.join(here, "profiles", "hbm_traffic.txt")) as fh:
+            for line in fh:
+                f = line.split()
+                if len(f) == 5 and not line.startswith("#") and f[0] == key and f[1] == workload and f[2] == sha:
+                    return int(f[3]) + int(f[4])
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(L, nb, logits_np, x_np, codes_np, sbits_np, fp8, budget_s, bytes_per_expert):
