@@ -40,6 +40,8 @@
 // (B) l % 32 for k = 16 s + 8 (l / 32) + j in step s; the 32x32 result sits
 // in lane l as column l % 32, rows 8 (j / 4) + 4 (l / 32) + j % 4.
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -113,6 +115,16 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
 }
 __device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory");
+}
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset (one VGPR per copy instead of a 64-bit address pair).
+__device__ __forceinline__ void dma16s(uint32_t off, const void* base, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory");
+}
+__device__ __forceinline__ void dma4s(uint32_t off, const void* base, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory");
 }
 
 // LDS stage layouts. A: 128 rows x 64 bf16 (128 B, 8 pieces of 16 B), piece
@@ -335,7 +347,306 @@ k_gateup_gemm(const uint16_t* __restrict__ xa, const float* __restrict__ sx, int
   }
 }
 
+// ---------------------------------------------------------------------------
+// int8, tall passes: 256 pairs x 128 gate (+128 up) columns per unit and pass.
+//
+// The result is kept in units of the current group's scale: for column n,
+//   R = (sum over groups so far of s_g * P_g) / s_current,
+// so a new group only multiplies R by s_current / s_new (one multiply per
+// element, no second accumulator) and the MFMAs add that group's plain code
+// products P_g on top; the stored value is R * s_last. The ratio adds about
+// two float32 roundings per group. A zero scale keeps the current one and its
+// codes are masked to zero, so such a group contributes exactly nothing.
+// Freed of the second accumulator, each wave holds 4 m-tiles x (32 gate + 32
+// up) columns: every code it decodes feeds four MFMAs, and a prefill-sized
+// expert (up to 256 pairs) is covered in one pass, so its codes are read
+// once.
+//
+// Waves: wm = wave / 4 takes the m-tiles (32 pass rows each) 2a + wm, a < 4,
+// interleaved so that both waves sharing a SIMD have work when an expert
+// has about 128 pairs; wn = wave % 4 takes the gate columns 32 wn .. +31 of
+// the unit and the matching up columns. A wave with no live m-tile skips the
+// products (NA = 0), one with at most two computes two, else three or four.
+// Ring: 3 slots (A 32 KB, B 16 KB, scales 2 KB each), two stages in flight
+// while one is multiplied. Group 0's scales come with stage 0, group g + 1's
+// with the last stage of group g, where each m-tile is rescaled right after
+// its last product of the group (so the multiplies overlap the products of
+// the other tiles instead of starting the next group on their own).
+constexpr int kTThreads = 512;
+constexpr int kTRows = 256;
+constexpr int kTGate = 128;
+
+__shared__ __attribute__((aligned(16))) uint16_t tA0[kTRows * kStageK];
+__shared__ __attribute__((aligned(16))) uint16_t tA1[kTRows * kStageK];
+__shared__ __attribute__((aligned(16))) uint16_t tA2[kTRows * kStageK];
+__shared__ __attribute__((aligned(16))) uint8_t tB0[2 * kTGate * kStageK];
+__shared__ __attribute__((aligned(16))) uint8_t tB1[2 * kTGate * kStageK];
+__shared__ __attribute__((aligned(16))) uint8_t tB2[2 * kTGate * kStageK];
+// scales of the unit's 256 code rows for one group: B row r at 64 (r / 32) + r % 32
+__shared__ __attribute__((aligned(16))) uint32_t tC0[2 * kTRows];
+__shared__ __attribute__((aligned(16))) uint32_t tC1[2 * kTRows];
+__shared__ __attribute__((aligned(16))) uint32_t tC2[2 * kTRows];
+
+// Stage layouts, bank-conflict free for 16-byte reads by 16 consecutive
+// lanes (consecutive rows) over the 64 four-byte banks: A piece p (8 bf16)
+// of row r (128 bytes) at p ^ ((r >> 1) & 7); B piece p (16 codes) of row r
+// (64 bytes) at p ^ ((r >> 2) & 3). Within a 64-K stage, MFMA k-step s takes
+// k = 32 h + 8 s .. +7 in the lanes of half h, so a B lane reads one
+// contiguous 32-byte span (pieces 2h, 2h+1) and an A lane piece 4h + s; both
+// sides agree on every k.
+__device__ __forceinline__ int ta_pos(int row, int piece) { return piece ^ ((row >> 1) & 7); }
+__device__ __forceinline__ int tb_pos(int row, int piece) { return piece ^ ((row >> 2) & 3); }
+
+// s_waitcnt vmcnt(n) for a count known only at run time (uniform, 0..8)
+__device__ __forceinline__ void wait_vm_dyn(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(wait_vm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(wait_vm(1)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(wait_vm(2)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(wait_vm(3)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(wait_vm(4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(wait_vm(5)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(wait_vm(6)); break;
+    case 7: __builtin_amdgcn_s_waitcnt(wait_vm(7)); break;
+    default: __builtin_amdgcn_s_waitcnt(wait_vm(8)); break;
+  }
+}
+
+template <int NA>
+struct TallPass {
+  f32x16 R[4][2];
+};
+
+__global__ void __launch_bounds__(kTThreads)
+k_gateup_gemm_tall(const uint16_t* __restrict__ xa, int K, const uint8_t* __restrict__ codes,
+                   const uint16_t* __restrict__ scales, int E, int N, int k,
+                   const int32_t* __restrict__ expert_off, const int32_t* __restrict__ sorted_pairs,
+                   float* __restrict__ gu, float* __restrict__ act, int ntiles) {
+  const int blk = blockIdx.x;
+  const int slot = blk / kXcds;
+  const int e = (blk % kXcds) + kXcds * (slot / ntiles);
+  const int nt = slot % ntiles;
+  if (e >= E) return;
+  const int r0 = expert_off[e];
+  const int m_e = expert_off[e + 1] - r0;
+  if (m_e <= 0) return;
+
+  const int I = N / 2, G = K / kGroup;
+  const int S = 2 * G;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int col = lane % 32, half = lane / 32;
+  const int wm = wave / 4, wn = wave % 4;
+  const int i0 = nt * kTGate + 32 * wn;
+  const bool live = i0 < I;
+  const int rg = 32 * wn + col, ru = kTGate + 32 * wn + col;  // this lane's code rows in a B stage
+  const uint32_t la0 = lds_addr(tA0), la1 = lds_addr(tA1), la2 = lds_addr(tA2);
+  const uint32_t lb0 = lds_addr(tB0), lb1 = lds_addr(tB1), lb2 = lds_addr(tB2);
+  const uint32_t lc0 = lds_addr(tC0), lc1 = lds_addr(tC1), lc2 = lds_addr(tC2);
+
+  // copies use per-block bases (SGPRs) and 32-bit byte offsets (N K < 2^31)
+  const uint8_t* cbase_p = codes + (size_t)e * N * K;
+  const int64_t sidx0 = ((int64_t)e * N * G) & ~(int64_t)1;         // dword-aligned first scale of e
+  const uint16_t* sbase_p = scales + sidx0;
+  // code rows this lane copies (instruction q: B rows 16 (2 wave + q) .. +15)
+  uint32_t boff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = 16 * (2 * wave + q) + lane / 4;
+    const int gi = nt * kTGate + (row % kTGate);
+    const int n = gi < I ? (row < kTGate ? gi : I + gi) : 0;
+    boff[q] = (uint32_t)n * (uint32_t)K + 16 * tb_pos(row, lane % 4);
+  }
+  // scale dword this lane copies: B row 32 wave + lane % 32 (lanes 32..63 repeat it);
+  // coff = element index of its group-0 scale relative to sidx0
+  uint32_t coff;
+  {
+    const int row = 32 * wave + (lane % 32);
+    const int gi = nt * kTGate + (row % kTGate);
+    const int n = gi < I ? (row < kTGate ? gi : I + gi) : 0;
+    coff = (uint32_t)(((int64_t)e * N + n) * G - sidx0);
+  }
+  const int par_g = (int)((((int64_t)e * N + (live ? i0 + col : 0)) * G) & 1);
+  const int par_u = (int)((((int64_t)e * N + (live ? I + i0 + col : 0)) * G) & 1);
+  const int cg_idx = 64 * (rg / 32) + (rg % 32), cu_idx = 64 * (ru / 32) + (ru % 32);
+  // LDS read offsets (bytes). The swizzles do not depend on the m-tile or on
+  // gate/up (rows 128 wm + 32 a + col and 32 wn + col (+128) share their low
+  // bits with col), so one base per A k-step and per B piece; m-tile (4096 a
+  // bytes) and up (8192 bytes) are immediates.
+  uint32_t aoffs[4], boffs[2];
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+    aoffs[st] = (uint32_t)((32 * wm + col) * (kStageK * 2) + 16 * ((4 * half + st) ^ ((col >> 1) & 7)));
+#pragma unroll
+  for (int pc = 0; pc < 2; ++pc) boffs[pc] = (uint32_t)(rg * kStageK + 16 * ((2 * half + pc) ^ ((col >> 2) & 3)));
+  auto half_bf16 = [](uint32_t w, int odd) { return __uint_as_float(odd ? (w & 0xffff0000u) : (w << 16)); };
+
+  for (int mb = 0; mb < m_e; mb += kTRows) {
+    const int rows = min(kTRows, m_e - mb);
+    const int mtiles = (rows + 31) / 32;                   // live m-tiles of the pass
+    const int na = live && mtiles > wm ? min(4, (mtiles - wm + 1) / 2) : 0;
+    // this wave copies A rows 32 wave .. +31 in four 8-row copies: only those
+    // holding pass rows (rows past the pass are never stored)
+    const int nca = min(4, max(0, (rows - 32 * wave + 7) / 8));
+    uint32_t aoff[4];  // byte offsets into x_rot
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 8 * (4 * wave + q) + lane / 8;
+      const int t = sorted_pairs[r0 + mb + min(row, rows - 1)] / k;
+      aoff[q] = 2u * ((uint32_t)t * (uint32_t)K + 8 * ta_pos(row, lane % 8));
+    }
+    // stages that bring scales: 0 (group 0) and 2g + 1 (group g + 1, if any)
+    auto has_c = [&](int h) { return h == 0 || ((h & 1) && (h + 1) / 2 < G); };
+    // copies per stage of this wave: A, 2 B, and the scales
+    auto dmas = [&](int h) { return nca + 2 + (has_c(h) ? 1 : 0); };
+
+    auto issue = [&](int h, uint32_t aslot, uint32_t bslot, uint32_t cslot) __attribute__((always_inline)) {
+      const uint32_t koff = (uint32_t)h * kStageK;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q < nca) dma16s(aoff[q] + 2u * koff, xa, aslot + (4 * wave + q) * (8 * kStageK * 2));
+#pragma unroll
+      for (int q = 0; q < 2; ++q) dma16s(boff[q] + koff, cbase_p, bslot + (2 * wave + q) * (16 * kStageK));
+      if (has_c(h)) dma4s(2u * ((coff + (h + 1) / 2) & ~1u), sbase_p, cslot + 4 * kWave * wave);
+    };
+
+    f32x16 R[4][2];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) R[a][c][j] = 0.0f;
+    float seff_g = 1.0f, seff_u = 1.0f;  // the scale R is currently expressed in
+    uint32_t mask_g = ~0u, mask_u = ~0u;
+    bool need_mask = false;
+
+    auto body = [&](auto na_c, int h, const uint16_t* abuf, const uint8_t* bbuf, const uint32_t* cbuf)
+        __attribute__((always_inline)) {
+      constexpr int NA = decltype(na_c)::value;
+      // scales of the group that starts next (read before this stage's products)
+      const bool next_c = (h & 1) && (h + 1) / 2 < G;
+      float sg = 0.0f, su = 0.0f;
+      if (h == 0 || next_c) {
+        const int g = (h + 1) / 2;
+        sg = half_bf16(cbuf[cg_idx], (par_g + g) & 1);
+        su = half_bf16(cbuf[cu_idx], (par_u + g) & 1);
+      }
+      if (h == 0) {
+        if (sg != 0.0f) seff_g = sg;
+        if (su != 0.0f) seff_u = su;
+        mask_g = sg != 0.0f ? ~0u : 0u;
+        mask_u = su != 0.0f ? ~0u : 0u;
+        need_mask = __ballot(sg == 0.0f || su == 0.0f) != 0;
+      }
+      u32x4 cgp[2], cup[2];  // the lane's 32 codes of its gate and up rows in this stage
+#pragma unroll
+      for (int pc = 0; pc < 2; ++pc) {
+        cgp[pc] = *reinterpret_cast<const u32x4*>(bbuf + boffs[pc]);
+        cup[pc] = *reinterpret_cast<const u32x4*>(bbuf + boffs[pc] + kTGate * kStageK);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4& cg4 = cgp[s / 2];
+        const u32x4& cu4 = cup[s / 2];
+        bf16x8 wg = decode8<WFmt::I8>(cg4[2 * (s % 2)], cg4[2 * (s % 2) + 1]);
+        bf16x8 wu = decode8<WFmt::I8>(cu4[2 * (s % 2)], cu4[2 * (s % 2) + 1]);
+        if (need_mask) {
+          u32x4 mg = __builtin_bit_cast(u32x4, wg), mu = __builtin_bit_cast(u32x4, wu);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            mg[w] &= mask_g;
+            mu[w] &= mask_u;
+          }
+          wg = __builtin_bit_cast(bf16x8, mg);
+          wu = __builtin_bit_cast(bf16x8, mu);
+        }
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint8_t*>(abuf) + aoffs[s] +
+                                                             64 * a * (kStageK * 2));
+          R[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, wg, R[a][0], 0, 0, 0);
+          R[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, wu, R[a][1], 0, 0, 0);
+        }
+      }
+      if (next_c) {
+        // express R in the next group's scale; a zero scale keeps the current one
+        const float rgt = sg != 0.0f ? seff_g / sg : 1.0f, rut = su != 0.0f ? seff_u / su : 1.0f;
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            R[a][0][j] *= rgt;
+            R[a][1][j] *= rut;
+          }
+        if (sg != 0.0f) seff_g = sg;
+        if (su != 0.0f) seff_u = su;
+        mask_g = sg != 0.0f ? ~0u : 0u;
+        mask_u = su != 0.0f ? ~0u : 0u;
+        need_mask = __ballot(sg == 0.0f || su == 0.0f) != 0;
+      }
+    };
+
+    auto stage = [&](auto na_c, int h, const uint16_t* abuf, const uint8_t* bbuf, const uint32_t* cbuf,
+                     uint32_t anext, uint32_t bnext, uint32_t cnext) __attribute__((always_inline)) {
+      if (h >= S) return;
+      // wait for this wave's copies of stage h (those of stage h + 1 may stay in flight)
+      wait_vm_dyn(h + 1 < S ? dmas(h + 1) : 0);
+      __builtin_amdgcn_s_barrier();            // ... and every other wave's
+      if (h + 2 < S) issue(h + 2, anext, bnext, cnext);  // the slot of stage h - 1, now free
+      constexpr int NA = decltype(na_c)::value;
+      if constexpr (NA > 0) body(na_c, h, abuf, bbuf, cbuf);
+    };
+
+    auto run = [&](auto na_c) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_barrier();  // nobody still reads the ring of the previous pass
+      issue(0, la0, lb0, lc0);
+      if (S > 1) issue(1, la1, lb1, lc1);
+      for (int hb = 0; hb < S; hb += 3) {       // stage h uses slot h % 3, fixed at compile time
+        stage(na_c, hb + 0, tA0, tB0, tC0, la2, lb2, lc2);
+        stage(na_c, hb + 1, tA1, tB1, tC1, la0, lb0, lc0);
+        stage(na_c, hb + 2, tA2, tB2, tC2, la1, lb1, lc1);
+      }
+    };
+    if (na > 3) run(std::integral_constant<int, 4>{});
+    else if (na > 2) run(std::integral_constant<int, 3>{});
+    else if (na > 0) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 0>{});
+
+    if (na > 0) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        if (a >= na) break;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int m = 32 * (2 * a + wm) + 8 * (j / 4) + 4 * half + (j % 4);
+          if (m < rows) {
+            const size_t r = (size_t)(r0 + mb + m);
+            const float gv = R[a][0][j] * seff_g, uv = R[a][1][j] * seff_u;
+            if (gu) {
+              gu[r * N + i0 + col] = gv;
+              gu[r * N + I + i0 + col] = uv;
+            }
+            if (act) act[r * I + i0 + col] = gelu_tanh(gv) * uv;
+          }
+        }
+      }
+    }
+  }
+}
+
 static int gemm_grid(int E, int ntiles) { return cdiv(E, kXcds) * kXcds * ntiles; }
+
+hipError_t launch_gateup_i8h_gemm_tall(const uint16_t* xrot, int T, int K, const int8_t* codes,
+                                       const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
+                                       const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st) {
+  (void)T;
+  int ntiles = cdiv(N / 2, kTGate);
+  k_gateup_gemm_tall<<<gemm_grid(E, ntiles), kTThreads, 0, st>>>(
+      xrot, K, reinterpret_cast<const uint8_t*>(codes), scales, E, N, k, expert_off, sorted_pairs, gu, act,
+      ntiles);
+  return hipGetLastError();
+}
 
 hipError_t launch_gateup_i8h_gemm(const uint16_t* xrot, int T, int K, const int8_t* codes,
                                   const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,

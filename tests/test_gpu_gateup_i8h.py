@@ -22,7 +22,7 @@ from tests.gpu_util import (assert_close, bf16_bits_of, bf16_cuda, check_with_ro
 
 pytestmark = pytest.mark.gpu
 
-PATHS = ("gemv", "gemm")
+PATHS = ("gemv", "gemm", "tall")
 
 
 def quantized_layer(L):
@@ -162,10 +162,30 @@ def test_edge_shapes(gpu_available, path, T, K, E, k, N):
     compare(gu, act, x, codes, sb, r["expert_off"], r["sorted_pairs"], k, what=f"edge/{path}")
 
 
-def test_gemm_only_large_k(gpu_available):
+@pytest.mark.parametrize("path", ("auto", "tall"))
+def test_gemm_only_large_k(gpu_available, path):
     x, xb, codes, sb, r = _random_case(6, 8192, 3, 2, 128, seed=11)
-    gu, act = run_gpu(xb, codes, sb, r["expert_off"], r["sorted_pairs"], 2, "auto")
-    compare(gu, act, x, codes, sb, r["expert_off"], r["sorted_pairs"], 2, what="K8192")
+    gu, act = run_gpu(xb, codes, sb, r["expert_off"], r["sorted_pairs"], 2, path)
+    compare(gu, act, x, codes, sb, r["expert_off"], r["sorted_pairs"], 2, what=f"K8192/{path}")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_zero_scales_with_nonzero_codes(gpu_available, path):
+    # a zero scale removes its group whatever the codes: single groups, a
+    # group zero for every row, whole rows of zeros, the first and the last
+    # group (the tall kernel keeps the running result in units of the last
+    # nonzero scale and masks such groups)
+    x, xb, codes, sb, r = _random_case(40, 1024, 4, 2, 256, seed=13)
+    s = numfmt.bf16_from_bits(sb).copy()
+    rng = np.random.default_rng(14)
+    s[rng.random(s.shape) < 0.1] = 0.0
+    s[:, :, 0] = 0.0          # the first group of every row
+    s[1, :, 7] = 0.0          # the last group of one expert
+    s[2, 5, :] = 0.0          # a whole row
+    s[3, 17, 1:] = 0.0        # only the first group left
+    sb = numfmt.bf16_to_bits(s)
+    gu, act = run_gpu(xb, codes, sb, r["expert_off"], r["sorted_pairs"], 2, path)
+    compare(gu, act, x, codes, sb, r["expert_off"], r["sorted_pairs"], 2, what=f"zero-scales/{path}")
 
 
 @pytest.mark.parametrize("path", PATHS)
