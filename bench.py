@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="weight copies cycled (0: enough to defeat caches)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm"])
+    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm", "tall"])
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 4 times (the reference kernel "
                          "whose FETCH_SIZE / WRITE_SIZE counters scale the HBM traffic figures)")
@@ -232,6 +232,8 @@ def main():
     elif args.path == "gemv" or (args.path == "auto" and L.T <= 8):
         kernel_name = "k_gateup_i8h_gemv" + ("<rotation fused>" if fused else "")
         key = "gemv_rot" if fused else "gemv"
+    elif args.path == "tall" or (args.path == "auto" and L.P >= 32 * L.E):
+        kernel_name, key = "k_gateup_gemm_tall (int8, 256-pair passes)", "gemm_tall"
     else:
         kernel_name, key = "k_gateup_gemm<I8>", "gemm_i8"
     traffic = measured_traffic(key, name)
@@ -273,13 +275,15 @@ def main():
     print(json.dumps(out))
 
 
-# source files of each timed kernel: a traffic figure holds only for the sources it was measured on
+# device-code sources of each timed kernel: a traffic figure holds only for the sources it was
+# measured on (launch.hpp only declares host launchers and is left out)
 KERNEL_SOURCES = {
-    "route_gateup_decode": ["gateup_i8h_gemv.hip", "topk.hpp", "xlane.hpp", "common.hpp", "launch.hpp"],
-    "gemv": ["gateup_i8h_gemv.hip", "topk.hpp", "xlane.hpp", "common.hpp", "launch.hpp"],
-    "gemv_rot": ["gateup_i8h_gemv.hip", "topk.hpp", "xlane.hpp", "common.hpp", "launch.hpp"],
-    "gemm_i8": ["gateup_gemm.hip", "common.hpp", "launch.hpp"],
-    "gemm_e4m3": ["gateup_gemm.hip", "gateup_fp8.hip", "xlane.hpp", "common.hpp", "launch.hpp"],
+    "route_gateup_decode": ["gateup_i8h_gemv.hip", "topk.hpp", "xlane.hpp", "common.hpp"],
+    "gemv": ["gateup_i8h_gemv.hip", "topk.hpp", "xlane.hpp", "common.hpp"],
+    "gemv_rot": ["gateup_i8h_gemv.hip", "topk.hpp", "xlane.hpp", "common.hpp"],
+    "gemm_i8": ["gateup_gemm.hip", "common.hpp"],
+    "gemm_tall": ["gateup_gemm.hip", "common.hpp"],
+    "gemm_e4m3": ["gateup_gemm.hip", "gateup_fp8.hip", "xlane.hpp", "common.hpp"],
 }
 
 
