@@ -40,11 +40,15 @@ __device__ __forceinline__ float sbyte(uint32_t w) {
 
 // GELU, tanh approximation: v/2 (1 + tanh(z)) with z = sqrt(2/pi)(v + 0.044715 v^3).
 // Evaluated as v / (1 + exp(-2z)), the same function written without the
-// cancellation of 1 + tanh(z) for negative z.
+// cancellation of 1 + tanh(z) for negative z, with the hardware base-2
+// exponential and reciprocal (each about 1 ulp; exp(-2z) = 2^(-2 z log2 e),
+// whose argument rounding adds a relative error of about |2z| 2^-24): a few
+// float32 ulps in all, far inside the product's tolerance. Large |z| gives
+// the exact limits (2^+big = inf -> v * 0, 2^-big = 0 -> v).
 __device__ __forceinline__ float gelu_tanh(float v) {
-  const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  float z = c * (v + 0.044715f * v * v * v);
-  return v / (1.0f + expf(-2.0f * z));
+  const float c2 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  const float t = c2 * (v + 0.044715f * v * v * v);
+  return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
 
 __host__ __device__ constexpr inline int cdiv(int a, int b) { return (a + b - 1) / b; }
