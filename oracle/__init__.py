@@ -24,10 +24,12 @@ Modules:
              activation quantizers
   router   - top-k routing, expert histogram, exclusive scan, stable scatter
   gateup   - the grouped gate_up products and the GELU-tanh(gate)*up epilogue
+  down     - the bf16 grouped down projection and the weighted combine of a
+             token's k expert outputs (the step after the path)
 
 Every function here is pinned by tests/test_oracle_*.py against closed
 forms, invariants, library special cases or brute force; none is marked
 "parity unpinned".
 """
 
-from . import numfmt, hadamard, quant, router, gateup  # noqa: F401
+from . import numfmt, hadamard, quant, router, gateup, down  # noqa: F401

@@ -155,3 +155,19 @@ def synthetic_fp8(L, experts=None):
         s = (0.02 * 4.0 / 448.0) * np.exp(0.1 * r.standard_normal((L.N // 128, L.G))).astype(np.float32)
         scales.append(to_bf16_bits(s))
     return np.stack(codes), np.stack(scales)
+
+
+def down_weights_bf16(L, experts=None):
+    """bf16 bit patterns [E', K, I] of the experts' down projections (hidden K
+    rows of I = N / 2 inputs each), N(0, 0.02^2), for the listed experts (all
+    by default)."""
+    ex = range(L.E) if experts is None else experts
+    return np.stack([to_bf16_bits(_rng(L.seed, "W_down", e).standard_normal((L.K, L.I), dtype=np.float32)
+                                  * np.float32(0.02)) for e in ex])
+
+
+def act_f32(L, rows=None):
+    """float32 [rows, I] stand-in for the gate_up epilogue's output (the down
+    projection's input), N(0, 1); P rows by default."""
+    r = L.P if rows is None else rows
+    return _rng(L.seed, "act").standard_normal((r, L.I), dtype=np.float32)
