@@ -217,6 +217,50 @@ int moe_gateup_fp8blk_grouped(const uint16_t* x, int T, int K,
                               float* gate_up, float* act,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * The step after the path: bf16 grouped down projection of the routed
+ * experts, then the weighted combine of each token's topk outputs.
+ *
+ * The int8 card's model table (row "Weights") keeps the experts' down
+ * projections in bf16 as the checkpoint ships them; the pages show neither
+ * that product nor the merge, so: W_down[e] is [H, I] (H = the hidden size);
+ * the float32 act rows are rounded to bf16 (nearest even) for the product,
+ * which accumulates in float32 (bf16 x bf16 products are exact there);
+ *   y[r, h]   = sum_i W_down[e(r), h, i] * bf16(act[r, i])  (sorted row r)
+ *   out[t, h] = sum_j topk_w[t, j] * y[pair_pos[t*topk + j], h]  (slot order)
+ *
+ * act        [P, I] float32, expert-sorted rows (the act of the gate_up calls),
+ *            16-B aligned; I % 8 == 0
+ * w_down     [E, H, I] bf16 bits, 16-B aligned; H % 8 == 0
+ * topk_ids, topk_w, expert_off, pair_pos: as moe_route_permute wrote them
+ * out        [T, H] float32 out, 16-B aligned
+ * workspace  at least moe_down_bf16_workspace_size(T, I, H, topk) bytes,
+ *            256-B aligned: the bf16 act rows and y, for the many-pairs form
+ *            (unused, may be NULL, for the one-launch form)
+ * Forms: for up to 64 pairs (and I <= 1024) one launch computes out directly
+ * (a workgroup owns 8 rows h of a token and all its slots); otherwise act is
+ * rounded into the workspace, a grouped bf16 MFMA GEMM writes y there
+ * (needs I % 32 == 0, H % 256 == 0, P*I < 2^31) and a combine kernel merges
+ * the slots. Outside both: I8H_EUNSUPPORTED. Results agree to float32
+ * rounding order. */
+size_t moe_down_bf16_workspace_size(int T, int I, int H, int topk);
+int moe_down_bf16_combine(const float* act, int T, int I, const uint16_t* w_down,
+                          int E, int H, int topk,
+                          const int32_t* topk_ids, const float* topk_w,
+                          const int32_t* expert_off, const int32_t* pair_pos,
+                          float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same with the form chosen by the caller: I8H_DOWN_AUTO (as above),
+ * I8H_DOWN_GEMV (the one-launch form, any T; I <= 1024) or I8H_DOWN_GEMM (the
+ * GEMM + combine form; its limits above, workspace required). */
+enum { I8H_DOWN_AUTO = 0, I8H_DOWN_GEMV = 1, I8H_DOWN_GEMM = 2 };
+int moe_down_bf16_combine_path(const float* act, int T, int I, const uint16_t* w_down,
+                               int E, int H, int topk,
+                               const int32_t* topk_ids, const float* topk_w,
+                               const int32_t* expert_off, const int32_t* pair_pos,
+                               float* out, void* workspace, size_t workspace_bytes,
+                               int path, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,6 +14,8 @@ Functions (same names as the C entry points):
   moe_route_gateup_i8h_decode   routing + rotation + gate_up in one launch (few tokens)
   fp8_quantize_activations   per-token, per-128 E4M3 activation quantizer
   moe_gateup_fp8blk_grouped  grouped FP8 E4M3 128x128-block gate_up + epilogue
+  moe_down_bf16_combine      bf16 grouped down projection + weighted combine
+                             (the step after the path)
 """
 
 import ctypes
@@ -26,6 +28,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libi8h.so")
 
 I8H_OK, I8H_EINVAL, I8H_EUNSUPPORTED, I8H_EHIP = 0, -1, -2, -3
 PATHS = {"auto": 0, "gemv": 1, "gemm": 2, "tall": 3}
+DOWN_PATHS = {"auto": 0, "gemv": 1, "gemm": 2}
 
 _lib = None
 
@@ -60,6 +63,9 @@ def lib():
         "fp8_quantize_activations": (I, [P, I, I, P, P, P]),
         "moe_gateup_fp8blk_workspace_size": (SZ, [I, I]),
         "moe_gateup_fp8blk_grouped": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P, SZ, P]),
+        "moe_down_bf16_workspace_size": (SZ, [I, I, I, I]),
+        "moe_down_bf16_combine": (I, [P, I, I, P, I, I, I, P, P, P, P, P, P, SZ, P]),
+        "moe_down_bf16_combine_path": (I, [P, I, I, P, I, I, I, P, P, P, P, P, P, SZ, I, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -283,3 +289,37 @@ def fp8_workspace_views(workspace, T, K):
     sx = workspace[a:a + T * (K // 128) * 4].view(torch.float32).view(T, K // 128)
     xq = workspace[b:b + T * K * 2].view(torch.bfloat16).view(T, K)
     return qx, sx, xq
+
+
+def moe_down_bf16_combine(act, w_down, routing, out=None, workspace=None, path="auto"):
+    """bf16 grouped down projection of the expert-sorted act rows [P, I]
+    float32 (rounded to bf16 for the product) against w_down [E, H, I] bf16,
+    merged per token with the router weights: returns out [T, H] float32.
+    `routing` is moe_route_permute's dict (topk_ids, topk_w, expert_off,
+    pair_pos); `path` is "auto", "gemv" (one launch) or "gemm" (GEMM +
+    combine)."""
+    _dev(act, "act", torch.float32, 2)
+    _dev(w_down, "w_down", torch.bfloat16, 3)
+    ids = _dev(routing["topk_ids"], "topk_ids", torch.int32, 2)
+    tw = _dev(routing["topk_w"], "topk_w", torch.float32, 2)
+    off = _dev(routing["expert_off"], "expert_off", torch.int32, 1)
+    pos = _dev(routing["pair_pos"], "pair_pos", torch.int32, 1)
+    T, topk = ids.shape
+    P, I = act.shape
+    E, H, I2 = w_down.shape
+    if I2 != I or P != T * topk or tw.shape != ids.shape or off.numel() != E + 1 or pos.numel() != P:
+        raise ValueError("inconsistent shapes")
+    dev = act.device
+    need = lib().moe_down_bf16_workspace_size(T, I, H, topk)
+    if path != "gemv" and need > 0 and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    else:
+        _dev(out, "out", torch.float32, 2)
+        if tuple(out.shape) != (T, H):
+            raise ValueError(f"out must have shape {(T, H)}")
+    _check("moe_down_bf16_combine", lib().moe_down_bf16_combine_path(
+        _ptr(act), T, I, _ptr(w_down), E, H, topk, _ptr(ids), _ptr(tw), _ptr(off), _ptr(pos), _ptr(out),
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), DOWN_PATHS[path], _stream(dev)))
+    return out

@@ -86,6 +86,63 @@ struct Fp8Ws {
 
 }  // namespace
 
+// bf16 grouped down projection + weighted combine
+namespace {
+
+constexpr int kDownGemvMaxPairs = 64;   // AUTO: the one-launch form up to this many pairs
+constexpr int kDownGemvMaxI = 1024;     // the one-launch form keeps I/256 pieces per lane
+
+inline bool down_gemv_ok(int I, int H) { return I <= kDownGemvMaxI && (H % 8) == 0; }
+inline bool down_gemm_ok(int T, int I, int H, int topk) {
+  return (I % 32) == 0 && (H % 256) == 0 && (int64_t)T * topk * I < ((int64_t)1 << 31) &&
+         (int64_t)256 * I < ((int64_t)1 << 31);
+}
+
+struct DownWs {
+  size_t a16, y, total;
+  DownWs(int T, int I, int H, int topk) {
+    const size_t p = (size_t)T * topk;
+    a16 = round_up(p * I * 2, 256);
+    y = round_up(p * H * 4, 256);
+    total = a16 + y;
+  }
+};
+
+int down_combine(const float* act, int T, int I, const uint16_t* w_down, int E, int H, int topk,
+                 const int32_t* topk_ids, const float* topk_w, const int32_t* expert_off, const int32_t* pair_pos,
+                 float* out, void* workspace, size_t workspace_bytes, int path, void* stream) {
+  if (T < 0 || I <= 0 || (I % 8) != 0 || H <= 0 || (H % 8) != 0 || E <= 0 || topk <= 0) return I8H_EINVAL;
+  if (E > kMaxExperts || topk > kMaxTopk || topk > E) return I8H_EUNSUPPORTED;
+  if ((int64_t)T * topk >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;
+  if (path < I8H_DOWN_AUTO || path > I8H_DOWN_GEMM) return I8H_EINVAL;
+  if (T == 0) return I8H_OK;
+  if (!act || !w_down || !topk_ids || !topk_w || !expert_off || !pair_pos || !out) return I8H_EINVAL;
+  if (!aligned(act, 16) || !aligned(w_down, 16) || !aligned(out, 16)) return I8H_EINVAL;
+  if (!aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(expert_off, 4) || !aligned(pair_pos, 4))
+    return I8H_EINVAL;
+  const int64_t pairs = (int64_t)T * topk;
+  if (path == I8H_DOWN_AUTO) {
+    if (pairs <= kDownGemvMaxPairs && down_gemv_ok(I, H)) path = I8H_DOWN_GEMV;
+    else if (down_gemm_ok(T, I, H, topk)) path = I8H_DOWN_GEMM;
+    else if (down_gemv_ok(I, H)) path = I8H_DOWN_GEMV;
+    else return I8H_EUNSUPPORTED;
+  }
+  if (path == I8H_DOWN_GEMV) {
+    if (!down_gemv_ok(I, H)) return I8H_EUNSUPPORTED;
+    return from_hip(i8h::launch_down_gemv_combine(act, T, I, w_down, H, topk, topk_ids, topk_w, pair_pos, out,
+                                                  as_stream(stream)));
+  }
+  if (!down_gemm_ok(T, I, H, topk)) return I8H_EUNSUPPORTED;
+  const DownWs ws(T, I, H, topk);
+  if (!workspace || workspace_bytes < ws.total || !aligned(workspace, 256)) return I8H_EINVAL;
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  return from_hip(i8h::launch_down_gemm_combine(act, T, I, w_down, E, H, topk, topk_w, expert_off, pair_pos,
+                                                reinterpret_cast<uint16_t*>(base),
+                                                reinterpret_cast<float*>(base + ws.a16), out, as_stream(stream)));
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* i8h_status_string(int status) {
@@ -242,6 +299,28 @@ int moe_gateup_fp8blk_grouped(const uint16_t* x, int T, int K, const uint8_t* co
   if (e != hipSuccess) return I8H_EHIP;
   return from_hip(i8h::launch_gateup_fp8(xq, sx, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs,
                                          gate_up, act, as_stream(stream)));
+}
+
+// bf16 grouped down projection + weighted combine
+size_t moe_down_bf16_workspace_size(int T, int I, int H, int topk) {
+  if (T <= 0 || I <= 0 || H <= 0 || topk <= 0) return 0;
+  return DownWs(T, I, H, topk).total;
+}
+
+int moe_down_bf16_combine(const float* act, int T, int I, const uint16_t* w_down, int E, int H, int topk,
+                          const int32_t* topk_ids, const float* topk_w, const int32_t* expert_off,
+                          const int32_t* pair_pos, float* out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return down_combine(act, T, I, w_down, E, H, topk, topk_ids, topk_w, expert_off, pair_pos, out, workspace,
+                      workspace_bytes, I8H_DOWN_AUTO, stream);
+}
+
+int moe_down_bf16_combine_path(const float* act, int T, int I, const uint16_t* w_down, int E, int H, int topk,
+                               const int32_t* topk_ids, const float* topk_w, const int32_t* expert_off,
+                               const int32_t* pair_pos, float* out, void* workspace, size_t workspace_bytes,
+                               int path, void* stream) {
+  return down_combine(act, T, I, w_down, E, H, topk, topk_ids, topk_w, expert_off, pair_pos, out, workspace,
+                      workspace_bytes, path, stream);
 }
 
 }  // extern "C"

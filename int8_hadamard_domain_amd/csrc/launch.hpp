@@ -44,4 +44,12 @@ hipError_t launch_gateup_fp8(const uint16_t* xq, const float* sx, int T, int K, 
                              const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
                              const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st);
 
+// bf16 grouped down projection + weighted combine (down.hip)
+hipError_t launch_down_gemv_combine(const float* act, int T, int I, const uint16_t* w, int H, int k,
+                                    const int32_t* ids, const float* tw, const int32_t* pos, float* out,
+                                    hipStream_t st);
+hipError_t launch_down_gemm_combine(const float* act, int T, int I, const uint16_t* w, int E, int H, int k,
+                                    const float* tw, const int32_t* expert_off, const int32_t* pos,
+                                    uint16_t* a16, float* y, float* out, hipStream_t st);
+
 }  // namespace i8h

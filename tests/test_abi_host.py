@@ -33,7 +33,7 @@ def L():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -54,6 +54,10 @@ def test_workspace_sizes(L):
     assert L.moe_gateup_fp8blk_workspace_size(3, 128) == 512 + 256 + 768   # each part rounded to 256 B
     assert L.moe_gateup_i8h_fused_workspace_size(1, 2048) == 0          # rotation inside the decode kernel
     assert L.moe_gateup_i8h_fused_workspace_size(128, 2048) == 128 * 2048 * 2
+    # bf16 act rows, then y, each rounded to 256 B
+    assert L.moe_down_bf16_workspace_size(2048, 768, 2048, 8) == 16384 * 768 * 2 + 16384 * 2048 * 4
+    assert L.moe_down_bf16_workspace_size(1, 8, 8, 1) == 256 + 256
+    assert L.moe_down_bf16_workspace_size(0, 768, 2048, 8) == 0
 
 
 def route(L, T=8, E=16, k=2, ptr=A, ws=A, wsb=1 << 20):
@@ -150,3 +154,29 @@ def test_decode_validation(L):
     assert dec(L, gu=None, act=None) == EINVAL       # nothing to compute
     assert dec(L, x=ODD) == EINVAL
     assert dec(L, lg=ODD) == EINVAL
+
+
+def down(L, act=A, T=4, I=256, w=A, E=8, H=512, k=2, ids=A, tw=A, off=A, pos=A, out=A, ws=A, wsb=1 << 30,
+         path=0):
+    return L.moe_down_bf16_combine_path(act, T, I, w, E, H, k, ids, tw, off, pos, out, ws, wsb, path, None)
+
+
+def test_down_validation(L):
+    assert down(L, I=100) == EINVAL                   # I % 8
+    assert down(L, H=12) == EINVAL                    # H % 8
+    assert down(L, E=2000) == EUNSUP
+    assert down(L, k=3, E=2) == EUNSUP
+    assert down(L, path=5) == EINVAL
+    assert down(L, T=0) == OK
+    assert down(L, act=None) == EINVAL
+    assert down(L, pos=None) == EINVAL
+    assert down(L, act=ODD) == EINVAL
+    assert down(L, out=ODD) == EINVAL
+    assert down(L, I=2048, path=1) == EUNSUP          # the one-launch form keeps I <= 1024
+    assert down(L, I=200, path=2) == EUNSUP           # the GEMM form needs I % 32 == 0
+    assert down(L, H=520, path=2) == EUNSUP           # ... and H % 256 == 0
+    assert down(L, T=100, ws=None) == EINVAL          # AUTO takes the GEMM form: workspace needed
+    assert down(L, T=100, wsb=16) == EINVAL           # too small
+    assert down(L, T=100, ws=ctypes.c_void_p(0x10010)) == EINVAL   # not 256-B aligned
+    assert down(L, I=2048, H=520, T=100) == EUNSUP    # neither form applies
+    assert L.moe_down_bf16_combine(None, 4, 256, A, 8, 512, 2, A, A, A, A, A, A, 1 << 30, None) == EINVAL
