@@ -56,6 +56,10 @@ def parse():
     ap.add_argument("--unfused", action="store_true",
                     help="rotate with hadamard128_rotate, then moe_gateup_i8h_grouped (default for decode: "
                          "moe_gateup_i8h_grouped_fused, rotation inside the gate_up kernel)")
+    ap.add_argument("--stage", default="gate_up", choices=["gate_up", "down"],
+                    help="down: time the step after the path instead, moe_down_bf16_combine (bf16 grouped down "
+                         "projection + weighted combine) on the workload's token count, with the routing "
+                         "computed beforehand and synthetic float32 act rows")
     return ap.parse_args()
 
 
@@ -87,6 +91,9 @@ def main():
 
     name = args.workload
     L = synth.layer(name)
+    if args.stage == "down":
+        bench_down(args, L, dev)
+        return
     fp8 = name == "fp8"
     fused = (not fp8) and (not args.unfused) and args.path == "auto" and L.T <= 8
     one_launch = fused and not args.two_launch and L.P <= 64 and L.E <= 256 and L.K <= 4096
@@ -284,6 +291,8 @@ KERNEL_SOURCES = {
     "gemm_i8": ["gateup_gemm.hip", "common.hpp"],
     "gemm_tall": ["gateup_gemm.hip", "common.hpp"],
     "gemm_e4m3": ["gateup_gemm.hip", "gateup_fp8.hip", "xlane.hpp", "common.hpp"],
+    "down_gemv": ["down.hip", "xlane.hpp", "common.hpp"],
+    "down_gemm": ["down.hip", "xlane.hpp", "common.hpp"],
 }
 
 
@@ -307,6 +316,131 @@ def measured_traffic(key, workload):
     except OSError:
         pass
     return None
+
+
+def bench_down(args, L, dev):
+    """The step after the path on the workload's shapes: out[T, H] from the
+    expert-sorted act rows [P, I] float32 and W_down [E, H, I] bf16 (H = K)."""
+    import torch
+    import int8_hadamard_domain_amd as i8h
+    import synth
+
+    k, H, I = L.topk, L.K, L.I
+    per_copy = L.E * H * I * 2
+    copies = args.copies if args.copies > 0 else int(min(16, max(2, np.ceil(
+        1.6e9 / max(min(L.E, L.P) / L.E * per_copy, 1)))))
+    nb = 64 if L.T == 1 else (8 if L.T <= 128 else 4)
+    S = nb * copies // np.gcd(nb, copies)
+    while S > 256:
+        S //= 2
+    steps = max(S, (args.steps + S - 1) // S * S)
+    warm = max(S, (args.warmup + S - 1) // S * S)
+
+    t_setup = time.perf_counter()
+    LB = synth.layer(L.name, T=L.T * nb)
+    logits_np = synth.router_logits(LB).reshape(nb, L.T, L.E)
+    w_np = synth.down_weights_bf16(L)
+    w0 = torch.from_numpy(w_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    ws_ = [w0] + [w0.clone() for _ in range(copies - 1)]
+    act_np = synth.act_f32(LB).reshape(nb, L.P, I)
+    acts = torch.from_numpy(act_np).to(dev)
+    routes = [i8h.moe_route_permute(torch.from_numpy(logits_np[b]).to(dev), k) for b in range(nb)]
+    out = torch.empty((L.T, H), dtype=torch.float32, device=dev)
+    wsz = i8h.lib().moe_down_bf16_workspace_size(L.T, I, H, k)
+    work = torch.empty((max(wsz, 1),), dtype=torch.uint8, device=dev)
+    gemv = L.P <= 64
+
+    def step(i):
+        i8h.moe_down_bf16_combine(acts[i % nb], ws_[i % copies], routes[i % nb], out=out, workspace=work)
+
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for i in range(S):
+            step(i)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(S):
+            step(i)
+    torch.cuda.synchronize(dev)
+    touched = [int(np.count_nonzero(np.diff(routes[i % nb]["expert_off"].cpu().numpy()))) for i in range(S)]
+    setup_s = time.perf_counter() - t_setup
+    wbytes = np.array(touched, dtype=np.float64) * H * I * 2
+
+    for _ in range(warm // S):
+        g.replay()
+    torch.cuda.synchronize(dev)
+    st = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(st)
+    for _ in range(steps // S):
+        g.replay()
+    ev1.record(st)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    call_us = ev0.elapsed_time(ev1) * 1e3 / steps
+    value = wbytes.sum() * (steps // S) / wall / 1e9
+    # algorithmic bytes per call: touched W_down, act read once, out written, routing lists
+    alg = wbytes.mean() + L.P * I * 4 + L.T * H * 4 + L.P * 4 * 3 + (L.E + 1) * 4
+    achieved = alg / (call_us * 1e-6) / 1e9
+    flops = 2.0 * L.P * H * I
+    key = "down_gemv" if gemv else "down_gemm"
+    kernel = ("k_down_gemv_combine (one launch)" if gemv else
+              "k_f32_to_bf16 + k_down_gemm + k_down_combine (the call)")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(key, "down-" + L.name),
+                "kernel": kernel, "kernel_us": round(call_us, 3), "alg_bytes_per_launch": int(alg),
+                "mfma_tflops": round(flops / (call_us * 1e-6) / 1e12, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import down, router
+        try:
+            import threadpoolctl
+            cores = max([d.get("num_threads", 1) for d in threadpoolctl.threadpool_info()] + [1])
+        except Exception:
+            cores = 1
+        wf = synth.bf16_bits_to_f64(w_np)
+        done, wb, tok = 0, 0.0, 0
+        c0 = time.perf_counter()
+        while time.perf_counter() - c0 < args.cpu_seconds and done < nb:
+            r = router.route(logits_np[done], k)
+            down.down_combine(act_np[done], wf, r["expert_off"], r["pair_pos"], r["weights"], k)
+            wb += np.count_nonzero(np.diff(r["expert_off"])) * H * I * 2
+            tok += L.T
+            done += 1
+        el = time.perf_counter() - c0
+        cpu = {"value": round(wb / el / 1e9, 4), "unit": "GB/s", "tokens_per_s": round(tok / el, 3),
+               "cores": int(cores), "kind": "oracle",
+               "sample": f"{done} step(s) of the same workload (route + down projection + combine, fp64 "
+                         f"NumPy), {el:.1f} s"}
+
+    print(json.dumps({
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "tokens_per_s": round(L.T * steps / wall, 1),
+        "n_gpus": 1,
+        "steps": int(steps),
+        "warmup": int(warm),
+        "ms_per_step": round(wall / steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16*bf16->f32",
+        "data": "synthetic",
+        "config": {"workload": f"down-{L.name}: T={L.T} H={H} I={I} E={L.E} top-{k} (down projection + "
+                               f"combine of Gemma 4 26B-A4B)",
+                   "T": L.T, "H": H, "I": I, "E": L.E, "topk": k, "weight_copies": int(copies),
+                   "steps_per_graph": int(S), "touched_experts_per_step": float(np.mean(touched)),
+                   "setup_s": round(setup_s, 1),
+                   "step": "moe_down_bf16_combine (" + ("one launch" if gemv else "bf16 act, GEMM, combine") + ")"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }))
 
 
 def cpu_baseline(L, nb, logits_np, x_np, codes_np, sbits_np, fp8, budget_s, bytes_per_expert):

@@ -143,8 +143,17 @@ constexpr int dg_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | 
 // 16 bytes per lane global -> LDS (M0 = the wave's LDS base, lane l's bytes at
 // base + 16 l), with a wave-uniform 64-bit base and a 32-bit lane offset. The
 // compiler neither counts nor waits on it; the kernel waits with vmcnt.
+// The base goes through readfirstlane: it is uniform, but the compiler does not
+// always prove it, and an "s" operand must be an SGPR.
 __device__ __forceinline__ void dg_dma16(uint32_t off, const void* base, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+  // (readfirstlane returns a signed int: take both halves as uint32_t before
+  // widening, or a low word with bit 31 set would sign-extend over the high one)
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t u = ((uint64_t)hi << 32) | lo;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off),
+               "s"(reinterpret_cast<const void*>(u)), "s"(lds)
                : "memory");
 }
 
