@@ -26,10 +26,12 @@ Modules:
   gateup   - the grouped gate_up products and the GELU-tanh(gate)*up epilogue
   down     - the bf16 grouped down projection and the weighted combine of a
              token's k expert outputs (the step after the path)
+  dense    - the drafter's dense int8 linears with f16 scales (RTN, no
+             transform) and their product
 
 Every function here is pinned by tests/test_oracle_*.py against closed
 forms, invariants, library special cases or brute force; none is marked
 "parity unpinned".
 """
 
-from . import numfmt, hadamard, quant, router, gateup, down  # noqa: F401
+from . import numfmt, hadamard, quant, router, gateup, down, dense  # noqa: F401

@@ -5,6 +5,10 @@ the int8 card (model table, row "Weights": one bf16 scale per row and 128 of
 K) and of the FP8 card (one bf16 scale per 128x128 block), and the rotated
 activations.
 
+f16 (IEEE binary16): 1 sign, 5 exponent (bias 15), 10 stored mantissa bits;
+the scales of the DFlash drafter's int8 linears on the int8 card (model
+table, row "Speculator": an f16 scale per row and 128 of K).
+
 E4M3: the FP8 card's weight codes (model table, row "Weights": FP8 E4M3).
 Read as the OCP "E4M3FN" flavour: 1 sign, 4 exponent (bias 7), 3 mantissa
 bits, no infinities, S.1111.111 is NaN, largest finite 448.
@@ -19,6 +23,10 @@ import numpy as np
 BF16_MANT_BITS = 7          # stored bits; 8 significant bits with the hidden one
 BF16_EMIN = -126            # exponent of the smallest normal
 BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+F16_MANT_BITS = 10
+F16_EMIN = -14
+F16_MAX = 65504.0           # (2 - 2**-10) * 2**15
 
 E4M3_MAX = 448.0            # 1.75 * 2**8
 E4M3_EMIN = -6              # exponent of the smallest normal (bias 7)
@@ -63,6 +71,43 @@ def bf16_from_bits(b):
     """fp64 value of bf16 bit patterns (uint16)."""
     b = np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16
     return b.view(np.float32).astype(np.float64)
+
+
+def f16_round(x):
+    """Nearest binary16 value of fp64 x (ties to even), as fp64; values that
+    reach max + half an ulp (65520) become inf."""
+    r = _round_to_quantum(x, F16_EMIN, F16_MANT_BITS)
+    big = np.abs(r) > F16_MAX
+    return np.where(big, np.copysign(np.inf, r), r)
+
+
+def f16_to_bits(v):
+    """uint16 bit pattern of binary16-representable fp64 values, from the
+    fields: sign, biased exponent (0 for subnormals), 10 mantissa bits."""
+    v = np.asarray(v, dtype=np.float64)
+    sign = np.signbit(v).astype(np.int64) << 15
+    a = np.abs(v)
+    bits = np.zeros(a.shape, dtype=np.int64)
+    inf = np.isinf(a)
+    bits[inf] = 0x1F << 10
+    nz = (a > 0) & ~inf
+    m, ex = np.frexp(a[nz])             # a = m * 2**ex, 0.5 <= m < 1
+    e = ex - 1
+    normal = e >= F16_EMIN
+    ef = np.where(normal, e + 15, 0)
+    mf = np.where(normal, np.rint((2.0 * m - 1.0) * 1024.0), np.rint(a[nz] / 2.0 ** (F16_EMIN - 10)))
+    bits[nz] = (ef << 10) | mf.astype(np.int64)
+    return (bits | sign).astype(np.uint16)
+
+
+def f16_from_bits(b):
+    """fp64 value of binary16 bit patterns (finite or inf; no NaN handling)."""
+    c = np.asarray(b, dtype=np.uint16).astype(np.int64)
+    sign = np.where(c & 0x8000, -1.0, 1.0)
+    ef = (c >> 10) & 0x1F
+    mf = c & 0x3FF
+    val = np.where(ef == 0, np.ldexp(mf / 1024.0, F16_EMIN), np.ldexp(1.0 + mf / 1024.0, ef - 15))
+    return sign * np.where(ef == 0x1F, np.inf, val)
 
 
 def e4m3_decode(codes):
