@@ -56,10 +56,12 @@ def parse():
     ap.add_argument("--unfused", action="store_true",
                     help="rotate with hadamard128_rotate, then moe_gateup_i8h_grouped (default for decode: "
                          "moe_gateup_i8h_grouped_fused, rotation inside the gate_up kernel)")
-    ap.add_argument("--stage", default="gate_up", choices=["gate_up", "down"],
+    ap.add_argument("--stage", default="gate_up", choices=["gate_up", "down", "linear"],
                     help="down: time the step after the path instead, moe_down_bf16_combine (bf16 grouped down "
                          "projection + weighted combine) on the workload's token count, with the routing "
-                         "computed beforehand and synthetic float32 act rows")
+                         "computed beforehand and synthetic float32 act rows; linear: the drafter's dense int8 "
+                         "linear with f16 group scales (linear_i8f16) on its stand-in shape, 16 tokens x "
+                         "K 2048 -> N 4096 (--workload is ignored)")
     return ap.parse_args()
 
 
@@ -93,6 +95,9 @@ def main():
     L = synth.layer(name)
     if args.stage == "down":
         bench_down(args, L, dev)
+        return
+    if args.stage == "linear":
+        bench_linear(args, dev)
         return
     fp8 = name == "fp8"
     fused = (not fp8) and (not args.unfused) and args.path == "auto" and L.T <= 8
@@ -293,6 +298,7 @@ KERNEL_SOURCES = {
     "gemm_e4m3": ["gateup_gemm.hip", "gateup_fp8.hip", "xlane.hpp", "common.hpp"],
     "down_gemv": ["down.hip", "xlane.hpp", "common.hpp"],
     "down_gemm": ["down.hip", "xlane.hpp", "common.hpp"],
+    "linear": ["linear.hip", "common.hpp"],
 }
 
 
@@ -439,6 +445,104 @@ def bench_down(args, L, dev):
                    "setup_s": round(setup_s, 1),
                    "step": "moe_down_bf16_combine (" + ("one launch" if gemv else "bf16 act, GEMM, combine") + ")"},
         "roofline": roofline,
+        "cpu_baseline": cpu,
+    }))
+
+
+def bench_linear(args, dev):
+    """The drafter's dense int8 linear with f16 group scales on its stand-in
+    shape (16 tokens, K 2048, N 4096); weight copies cycled past the caches."""
+    import torch
+    import int8_hadamard_domain_amd as i8h
+    import synth
+
+    d = synth.DRAFTER
+    T, K, N = d["T"], d["K"], d["N"]
+    wbytes = N * K + N * (K // 128) * 2
+    copies = args.copies if args.copies > 0 else int(min(256, max(2, np.ceil(1.6e9 / wbytes))))
+    S = copies
+    steps = max(S, (args.steps + S - 1) // S * S)
+    warm = max(S, (args.warmup + S - 1) // S * S)
+    t_setup = time.perf_counter()
+    q_np, s_np = synth.synthetic_i8f16(N, K, d["seed"])
+    x_np = synth.drafter_activations_bf16(T, K, d["seed"])
+    q0 = torch.from_numpy(q_np).to(dev)
+    s0 = torch.from_numpy(s_np.view(np.int16)).view(torch.float16).to(dev)
+    qs = [q0] + [q0.clone() for _ in range(copies - 1)]
+    ss = [s0] + [s0.clone() for _ in range(copies - 1)]
+    x = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    y = torch.empty((T, N), dtype=torch.float32, device=dev)
+
+    def step(i):
+        i8h.linear_i8f16(x, qs[i % copies], ss[i % copies], out=y)
+
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for i in range(S):
+            step(i)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(S):
+            step(i)
+    torch.cuda.synchronize(dev)
+    setup_s = time.perf_counter() - t_setup
+    for _ in range(warm // S):
+        g.replay()
+    torch.cuda.synchronize(dev)
+    st = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(st)
+    for _ in range(steps // S):
+        g.replay()
+    ev1.record(st)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    call_us = ev0.elapsed_time(ev1) * 1e3 / steps
+    alg = wbytes + T * K * 2 + T * N * 4
+    achieved = alg / (call_us * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import dense, numfmt
+        try:
+            import threadpoolctl
+            cores = max([dd.get("num_threads", 1) for dd in threadpoolctl.threadpool_info()] + [1])
+        except Exception:
+            cores = 1
+        xf, sf = synth.bf16_bits_to_f64(x_np), numfmt.f16_from_bits(s_np)
+        done = 0
+        c0 = time.perf_counter()
+        while time.perf_counter() - c0 < args.cpu_seconds and done < 64:
+            dense.linear_i8_f16(xf, q_np, sf)
+            done += 1
+        el = time.perf_counter() - c0
+        cpu = {"value": round(done * wbytes / el / 1e9, 4), "unit": "GB/s", "tokens_per_s": round(done * T / el, 3),
+               "cores": int(cores), "kind": "oracle",
+               "sample": f"{done} call(s) of the same linear (fp64 NumPy), {el:.1f} s"}
+    print(json.dumps({
+        "metric": METRIC,
+        "value": round(wbytes * steps / wall / 1e9, 2),
+        "unit": "GB/s",
+        "tokens_per_s": round(T * steps / wall, 1),
+        "n_gpus": 1,
+        "steps": int(steps),
+        "warmup": int(warm),
+        "ms_per_step": round(wall / steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8*bf16->f32",
+        "data": "synthetic",
+        "config": {"workload": f"drafter linear stand-in: T={T} K={K} N={N} (int8, f16 scale per row per 128)",
+                   "T": T, "K": K, "N": N, "weight_copies": int(copies), "setup_s": round(setup_s, 1),
+                   "step": "linear_i8f16"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("linear", "drafter"),
+                     "kernel": "k_linear_i8f16", "kernel_us": round(call_us, 3), "alg_bytes_per_launch": int(alg),
+                     "mfma_tflops": round(2.0 * T * N * K / (call_us * 1e-6) / 1e12, 2)},
         "cpu_baseline": cpu,
     }))
 

@@ -261,6 +261,21 @@ int moe_down_bf16_combine_path(const float* act, int T, int I, const uint16_t* w
                                float* out, void* workspace, size_t workspace_bytes,
                                int path, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Dense int8 linear with an f16 scale per row and 128 of K, no transform: the
+ * DFlash drafter's linears and head on the int8 card (model table, row
+ * "Speculator"; recipe lines `rtn codes=i8 group=128 scale=f16 clamp=sym`).
+ *   y[t, n] = sum_g scales[n, g] * sum_{k in g} codes[n, k] * x[t, k]
+ * x       [T, K] bf16 bits (unrotated), 16-B aligned; K % 128 == 0
+ * codes   [N, K] int8 in -127..127, 16-B aligned; N % 16 == 0
+ * scales  [N, K/128] f16 bits (IEEE binary16), 2-B aligned
+ * y       [T, N] float32 out, 4-B aligned
+ * Products exact in float32, float32 accumulation. Made for the drafter's
+ * blocks of 16 positions: a workgroup owns 16 columns x 16 tokens, so larger
+ * T re-reads the codes once per 16 tokens. No workspace. */
+int linear_i8f16(const uint16_t* x, int T, int K, const int8_t* codes, const uint16_t* scales,
+                 int N, float* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

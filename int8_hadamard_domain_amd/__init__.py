@@ -16,6 +16,8 @@ Functions (same names as the C entry points):
   moe_gateup_fp8blk_grouped  grouped FP8 E4M3 128x128-block gate_up + epilogue
   moe_down_bf16_combine      bf16 grouped down projection + weighted combine
                              (the step after the path)
+  linear_i8f16               dense int8 linear with f16 group scales (the
+                             drafter's linears)
 """
 
 import ctypes
@@ -66,6 +68,7 @@ def lib():
         "moe_down_bf16_workspace_size": (SZ, [I, I, I, I]),
         "moe_down_bf16_combine": (I, [P, I, I, P, I, I, I, P, P, P, P, P, P, SZ, P]),
         "moe_down_bf16_combine_path": (I, [P, I, I, P, I, I, I, P, P, P, P, P, P, SZ, I, P]),
+        "linear_i8f16": (I, [P, I, I, P, P, I, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -322,4 +325,25 @@ def moe_down_bf16_combine(act, w_down, routing, out=None, workspace=None, path="
     _check("moe_down_bf16_combine", lib().moe_down_bf16_combine_path(
         _ptr(act), T, I, _ptr(w_down), E, H, topk, _ptr(ids), _ptr(tw), _ptr(off), _ptr(pos), _ptr(out),
         _ptr(workspace), 0 if workspace is None else workspace.numel(), DOWN_PATHS[path], _stream(dev)))
+    return out
+
+
+def linear_i8f16(x, codes, scales, out=None):
+    """Dense int8 linear: x [T, K] bf16 (unrotated), codes [N, K] int8,
+    scales [N, K/128] float16 -> y [T, N] float32."""
+    _dev(x, "x", torch.bfloat16, 2)
+    _dev(codes, "codes", torch.int8, 2)
+    _dev(scales, "scales", torch.float16, 2)
+    T, K = x.shape
+    N, K2 = codes.shape
+    if K2 != K or tuple(scales.shape) != (N, K // 128):
+        raise ValueError("inconsistent shapes")
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float32, device=dev)
+    else:
+        _dev(out, "out", torch.float32, 2)
+        if tuple(out.shape) != (T, N):
+            raise ValueError(f"out must have shape {(T, N)}")
+    _check("linear_i8f16", lib().linear_i8f16(_ptr(x), T, K, _ptr(codes), _ptr(scales), N, _ptr(out), _stream(dev)))
     return out

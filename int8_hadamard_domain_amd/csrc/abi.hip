@@ -323,4 +323,15 @@ int moe_down_bf16_combine_path(const float* act, int T, int I, const uint16_t* w
                       workspace_bytes, path, stream);
 }
 
+// dense int8 linear with f16 group scales (the drafter's linears)
+int linear_i8f16(const uint16_t* x, int T, int K, const int8_t* codes, const uint16_t* scales, int N, float* y,
+                 void* stream) {
+  if (T < 0 || K <= 0 || (K % 128) != 0 || N <= 0 || (N % 16) != 0) return I8H_EINVAL;
+  if ((int64_t)T * K >= (int64_t)1 << 31 || (int64_t)N * K >= ((int64_t)1 << 40)) return I8H_EUNSUPPORTED;
+  if (T == 0) return I8H_OK;
+  if (!x || !codes || !scales || !y) return I8H_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(y, 4)) return I8H_EINVAL;
+  return from_hip(i8h::launch_linear_i8f16(x, T, K, codes, scales, N, y, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -52,4 +52,8 @@ hipError_t launch_down_gemm_combine(const float* act, int T, int I, const uint16
                                     const float* tw, const int32_t* expert_off, const int32_t* pos,
                                     uint16_t* a16, float* y, float* out, hipStream_t st);
 
+// dense int8 linear with f16 group scales (linear.hip)
+hipError_t launch_linear_i8f16(const uint16_t* x, int T, int K, const int8_t* codes, const uint16_t* scales, int N,
+                               float* y, hipStream_t st);
+
 }  // namespace i8h

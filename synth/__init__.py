@@ -171,3 +171,30 @@ def act_f32(L, rows=None):
     projection's input), N(0, 1); P rows by default."""
     r = L.P if rows is None else rows
     return _rng(L.seed, "act").standard_normal((r, L.I), dtype=np.float32)
+
+
+def f16_bits(x32):
+    """float32 values -> IEEE binary16 bit patterns (nearest even), numpy's cast."""
+    return np.asarray(x32, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+# Stand-in for one of the DFlash drafter's linears (int8 card, model table row
+# "Speculator": it drafts 15 tokens a step, so it runs on blocks of 16
+# positions): 16 tokens, hidden 2048 in, 4096 out.
+DRAFTER = dict(T=16, K=2048, N=4096, seed=6)
+
+
+def synthetic_i8f16(n_rows, k_dim, seed, stream="i8f16"):
+    """Directly drawn int8 codes [N, K] (-127..127) and f16 scale bits
+    [N, K/128] of the magnitude the RTN quantizer gives N(0, 0.02^2) rows
+    (amax about 3 sigma: s near 0.02 * 3 / 127)."""
+    r = _rng(seed, stream)
+    c = np.rint(r.standard_normal((n_rows, k_dim), dtype=np.float32) * np.float32(127.0 / 3.0))
+    codes = np.clip(c, -127, 127).astype(np.int8)
+    s = (0.02 * 3.0 / 127.0) * np.exp(0.1 * r.standard_normal((n_rows, k_dim // 128))).astype(np.float32)
+    return codes, f16_bits(s)
+
+
+def drafter_activations_bf16(T, K, seed):
+    """bf16 bit patterns [T, K], N(0, 1), for the drafter's linears."""
+    return to_bf16_bits(_rng(seed, "drafter_x").standard_normal((T, K), dtype=np.float32))

@@ -33,7 +33,7 @@ def L():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -180,3 +180,14 @@ def test_down_validation(L):
     assert down(L, T=100, ws=ctypes.c_void_p(0x10010)) == EINVAL   # not 256-B aligned
     assert down(L, I=2048, H=520, T=100) == EUNSUP    # neither form applies
     assert L.moe_down_bf16_combine(None, 4, 256, A, 8, 512, 2, A, A, A, A, A, A, 1 << 30, None) == EINVAL
+
+
+def test_linear_validation(L):
+    f = L.linear_i8f16
+    assert f(A, 4, 100, A, A, 64, A, None) == EINVAL          # K % 128
+    assert f(A, 4, 256, A, A, 24, A, None) == EINVAL          # N % 16
+    assert f(A, 0, 256, A, A, 64, A, None) == OK
+    assert f(None, 4, 256, A, A, 64, A, None) == EINVAL
+    assert f(ODD, 4, 256, A, A, 64, A, None) == EINVAL
+    assert f(A, 4, 256, A, ctypes.c_void_p(0x10001), 64, A, None) == EINVAL   # scales 2-B aligned
+    assert f(A, 1 << 20, 4096, A, A, 64, A, None) == EUNSUP   # T*K offsets are 32-bit
