@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="weight copies cycled (0: enough to defeat caches)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm", "tall"])
+    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm", "tall", "skinny"])
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 4 times (the reference kernel "
                          "whose FETCH_SIZE / WRITE_SIZE counters scale the HBM traffic figures)")
@@ -246,8 +246,10 @@ def main():
         key = "gemv_rot" if fused else "gemv"
     elif args.path == "tall" or (args.path == "auto" and L.P >= 32 * L.E):
         kernel_name, key = "k_gateup_gemm_tall (int8, 256-pair passes)", "gemm_tall"
-    else:
+    elif args.path == "gemm":
         kernel_name, key = "k_gateup_gemm<I8>", "gemm_i8"
+    else:
+        kernel_name, key = "k_gateup_i8h_skinny (int8, 64-pair passes)", "skinny"
     traffic = measured_traffic(key, name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -299,6 +301,7 @@ KERNEL_SOURCES = {
     "down_gemv": ["down.hip", "xlane.hpp", "common.hpp"],
     "down_gemm": ["down.hip", "xlane.hpp", "common.hpp"],
     "linear": ["linear.hip", "common.hpp"],
+    "skinny": ["gateup_skinny.hip", "common.hpp"],
 }
 
 

@@ -130,14 +130,16 @@ int moe_gateup_i8h_grouped(const uint16_t* x_rot, int T, int K,
 
 /* Same as moe_gateup_i8h_grouped with the kernel chosen by the caller:
  * I8H_PATH_AUTO (as the call above: GEMV for T <= 8 and K <= 4096, TALL when
- * the pairs average at least 32 per expert, else GEMM), I8H_PATH_GEMV (the
+ * the pairs average at least 32 per expert, else SKINNY), I8H_PATH_GEMV (the
  * decode-shaped kernel: VALU dot products streaming codes with 16-byte
  * loads), I8H_PATH_GEMM (bf16 MFMA, passes of 128 pairs, a second
  * accumulator per 128-K group) or I8H_PATH_TALL (bf16 MFMA, passes of 256
- * pairs, the running result kept in units of the current group's scale).
+ * pairs, the running result kept in units of the current group's scale) or
+ * I8H_PATH_SKINNY (bf16 MFMA for few pairs per expert: passes of 64 pairs,
+ * units of 64 gate + 64 up columns, two workgroups per CU).
  * All give the same result to float32 rounding. TALL needs N*K < 2^31
  * (else I8H_EUNSUPPORTED). */
-enum { I8H_PATH_AUTO = 0, I8H_PATH_GEMV = 1, I8H_PATH_GEMM = 2, I8H_PATH_TALL = 3 };
+enum { I8H_PATH_AUTO = 0, I8H_PATH_GEMV = 1, I8H_PATH_GEMM = 2, I8H_PATH_TALL = 3, I8H_PATH_SKINNY = 4 };
 int moe_gateup_i8h_grouped_path(const uint16_t* x_rot, int T, int K,
                                 const int8_t* codes, const uint16_t* scales,
                                 int E, int N, int topk,

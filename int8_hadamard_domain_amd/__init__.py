@@ -29,7 +29,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libi8h.so")
 
 I8H_OK, I8H_EINVAL, I8H_EUNSUPPORTED, I8H_EHIP = 0, -1, -2, -3
-PATHS = {"auto": 0, "gemv": 1, "gemm": 2, "tall": 3}
+PATHS = {"auto": 0, "gemv": 1, "gemm": 2, "tall": 3, "skinny": 4}
 DOWN_PATHS = {"auto": 0, "gemv": 1, "gemm": 2}
 
 _lib = None

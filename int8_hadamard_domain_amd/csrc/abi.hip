@@ -35,11 +35,12 @@ inline bool auto_gemv(int T, int K) { return T <= kGemvMaxT && K <= kGemvMaxK; }
 // the tall kernel addresses one expert's codes with 32-bit offsets
 inline bool tall_fits(int K, int N) { return (int64_t)N * K < ((int64_t)1 << 31); }
 
-// kernel for the MFMA range: 256-pair passes once experts average 32 pairs
+// kernel for the MFMA range: 256-pair passes once experts average 32 pairs,
+// below that the small-unit kernel (64-pair passes, three workgroups a CU)
 inline int auto_path(int T, int K, int E, int N, int topk) {
   if (auto_gemv(T, K)) return I8H_PATH_GEMV;
   if ((int64_t)T * topk >= (int64_t)32 * E && tall_fits(K, N)) return I8H_PATH_TALL;
-  return I8H_PATH_GEMM;
+  return I8H_PATH_SKINNY;
 }
 
 int gateup_i8h(const uint16_t* x_rot, int T, int K, const int8_t* codes, const uint16_t* scales, int E, int N,
@@ -48,8 +49,7 @@ int gateup_i8h(const uint16_t* x_rot, int T, int K, const int8_t* codes, const u
   int rc = check_common_moe(T, K, E, N, topk);
   if (rc != I8H_OK) return rc;
   if ((N % 64) != 0) return I8H_EINVAL;
-  if (path != I8H_PATH_AUTO && path != I8H_PATH_GEMV && path != I8H_PATH_GEMM && path != I8H_PATH_TALL)
-    return I8H_EINVAL;
+  if (path < I8H_PATH_AUTO || path > I8H_PATH_SKINNY) return I8H_EINVAL;
   if (T == 0) return I8H_OK;
   if (!x_rot || !codes || !scales || !expert_off || !sorted_pairs) return I8H_EINVAL;
   if (!aligned(x_rot, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return I8H_EINVAL;
@@ -66,6 +66,9 @@ int gateup_i8h(const uint16_t* x_rot, int T, int K, const int8_t* codes, const u
   else if (path == I8H_PATH_TALL)
     e = i8h::launch_gateup_i8h_gemm_tall(x_rot, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs,
                                          gate_up, act, as_stream(stream));
+  else if (path == I8H_PATH_SKINNY)
+    e = i8h::launch_gateup_i8h_skinny(x_rot, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up,
+                                      act, as_stream(stream));
   else
     e = i8h::launch_gateup_i8h_gemm(x_rot, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up,
                                     act, as_stream(stream));
@@ -249,8 +252,8 @@ int moe_gateup_i8h_grouped_fused(const uint16_t* x, int T, int K, const int8_t* 
   if (auto_path(T, K, E, N, topk) == I8H_PATH_TALL)
     return from_hip(i8h::launch_gateup_i8h_gemm_tall(xr, T, K, codes, scales, E, N, topk, expert_off,
                                                       sorted_pairs, gate_up, act, st));
-  return from_hip(i8h::launch_gateup_i8h_gemm(xr, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs,
-                                               gate_up, act, st));
+  return from_hip(i8h::launch_gateup_i8h_skinny(xr, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs,
+                                                gate_up, act, st));
 }
 
 int moe_route_gateup_i8h_decode(const float* logits, const uint16_t* x, int T, int K, const int8_t* codes,

@@ -22,7 +22,7 @@ from tests.gpu_util import (assert_close, bf16_bits_of, bf16_cuda, check_with_ro
 
 pytestmark = pytest.mark.gpu
 
-PATHS = ("gemv", "gemm", "tall")
+PATHS = ("gemv", "gemm", "tall", "skinny")
 
 
 def quantized_layer(L):
