@@ -242,7 +242,7 @@ int moe_gateup_fp8blk_grouped(const uint16_t* x, int T, int K,
  * Forms: for up to 64 pairs (and I <= 1024) one launch computes out directly
  * (a workgroup owns 8 rows h of a token and all its slots); otherwise act is
  * rounded into the workspace, a grouped bf16 MFMA GEMM writes y there
- * (needs I % 32 == 0, H % 256 == 0, P*I < 2^31) and a combine kernel merges
+ * (needs I % 32 == 0, I >= 96, H % 256 == 0, P*I < 2^31) and a combine kernel merges
  * the slots. Outside both: I8H_EUNSUPPORTED. Results agree to float32
  * rounding order. */
 size_t moe_down_bf16_workspace_size(int T, int I, int H, int topk);

@@ -97,7 +97,7 @@ constexpr int kDownGemvMaxI = 1024;     // the one-launch form keeps I/256 piece
 
 inline bool down_gemv_ok(int I, int H) { return I <= kDownGemvMaxI && (H % 8) == 0; }
 inline bool down_gemm_ok(int T, int I, int H, int topk) {
-  return (I % 32) == 0 && (H % 256) == 0 && (int64_t)T * topk * I < ((int64_t)1 << 31) &&
+  return (I % 32) == 0 && I >= 96 && (H % 256) == 0 && (int64_t)T * topk * I < ((int64_t)1 << 31) &&
          (int64_t)256 * I < ((int64_t)1 << 31);
 }
 

@@ -17,10 +17,11 @@
 //     and are merged in slot order. No intermediate y, one launch.
 //   * many pairs (verify, prefill): act -> bf16 once, a grouped bf16 MFMA GEMM
 //     writes y in sorted order, then a combine kernel merges the k rows of
-//     each token. The GEMM unit is (expert, 256 output columns) x passes of
-//     256 sorted rows; 64-byte-per-row stages of A (act rows) and B (W_down
-//     rows) go global -> LDS by gfx950's DMA into a 4-slot ring, and eight
-//     waves (two per SIMD) each hold 4 m-tiles x 2 column tiles of
+//     each token. The GEMM is persistent: a workgroup per CU streams work
+//     items (expert, 256 output columns), each in passes of 256 sorted rows,
+//     back to back; 64-byte-per-row stages of A (act rows) and B (W_down rows)
+//     go global -> LDS by gfx950's DMA into a 4-slot ring, and eight waves
+//     (two per SIMD) each hold 4 m-tiles x 2 column tiles of
 //     v_mfma_f32_32x32x16_bf16 results.
 
 #include <type_traits>
@@ -135,6 +136,7 @@ constexpr int kDgASlot = kDgRows * kDgStageK * 2;   // 16 KB
 constexpr int kDgBSlot = kDgCols * kDgStageK * 2;   // 16 KB
 constexpr int kDgSlotBytes = kDgASlot + kDgBSlot;
 constexpr int kDgXcds = 8;
+constexpr int kDgBlocks = 256;               // one resident workgroup per CU
 
 __shared__ __attribute__((aligned(16))) uint8_t dRing[kDgSlots * kDgSlotBytes];
 
@@ -162,28 +164,54 @@ __device__ __forceinline__ void dg_dma16(uint32_t off, const void* base, uint32_
 // piece hit 64 distinct banks. (An involution: position -> piece alike.)
 __device__ __forceinline__ int dg_pos(int row, int piece) { return piece ^ ((row >> 2) & 3); }
 
+// s_waitcnt vmcnt(n) for a wave-uniform n known at run time (0..8)
+__device__ __forceinline__ void dg_wait_rt(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(dg_vm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(dg_vm(1)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(dg_vm(2)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(dg_vm(3)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(dg_vm(4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(dg_vm(5)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(dg_vm(6)); break;
+    case 7: __builtin_amdgcn_s_waitcnt(dg_vm(7)); break;
+    default: __builtin_amdgcn_s_waitcnt(dg_vm(8)); break;
+  }
+}
+
+__shared__ int32_t dEoff[kMaxExperts + 1];   // expert offsets, staged once
+
+// One pass: up to 256 consecutive sorted rows of expert e against column tile nt.
+struct DPass {
+  int e, nt, r0, mb, rows;
+};
+
+// Persistent: a workgroup takes work items (expert e, column tile nt) b, b +
+// grid, ... (the items of expert e on XCD e % 8, its column tiles on
+// consecutive workgroups so they read its A rows from one L2), each one or
+// more passes of 256 rows, and streams the passes' stages back to back: the
+// next pass's first three stages are copied during the current pass's last
+// three, and its y stores (which count in vmcnt) are issued after this wave
+// has waited for the next pass's first stage, so nothing drains between
+// passes. The A rows of a pass are contiguous (sorted order), so everything
+// a pass needs comes from the staged offsets: no global load mid-stream.
 __global__ void __launch_bounds__(kDgThreads)
 k_down_gemm(const uint16_t* __restrict__ a16, int I, const uint16_t* __restrict__ w, int E, int H,
             const int32_t* __restrict__ expert_off, float* __restrict__ y, int ntiles) {
-  // the column units of expert e run on XCD e % 8, consecutive in dispatch order
-  const int blk = blockIdx.x;
-  const int slot = blk / kDgXcds;
-  const int e = (blk % kDgXcds) + kDgXcds * (slot / ntiles);
-  const int nt = slot % ntiles;
-  if (e >= E) return;
-  const int r0 = expert_off[e];
-  const int m_e = expert_off[e + 1] - r0;
-  if (m_e <= 0) return;
-
-  const int S = I / kDgStageK;
+  const int S = I / kDgStageK;                 // stages per pass, at least 3
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / 4, wn = wave % 4;     // m-tiles 2a + wm; columns 64 wn .. +63
   const int col = lane % 32, half = lane / 32;
   const uint32_t ring = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)dRing);
+  const int nitems = cdiv(E, kDgXcds) * kDgXcds * ntiles;
+  const int grid = gridDim.x;
+
+  for (int i = tid; i <= E; i += kDgThreads) dEoff[i] = expert_off[i];
+  __syncthreads();
 
   // B copies: instruction q fills W_down rows nt*256 + 16 (2 wave + q) + lane / 4
-  const uint16_t* wbase = w + ((size_t)e * H + (size_t)nt * kDgCols) * I;
+  // (the same offsets for every item, from the item's row base)
   uint32_t boff[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -202,44 +230,81 @@ k_down_gemm(const uint16_t* __restrict__ a16, int I, const uint16_t* __restrict_
     }
   }
 
-  for (int mb = 0; mb < m_e; mb += kDgRows) {
-    const int rows = min(kDgRows, m_e - mb);
-    const int mtiles = (rows + 31) / 32;
-    const int na = (mtiles - wm + 1) / 2;     // live m-tiles 2a + wm of this wave
-    // A copies of this wave: instruction q fills pass rows 16 (2 wave + q) + lane / 4,
-    // only those blocks of 16 that hold pass rows (later rows repeat the last one)
-    uint32_t aoff[2];
+  auto first_pass = [&](int& it, DPass& p) __attribute__((always_inline)) {
+    for (; it < nitems; it += grid) {
+      const int slot = it / kDgXcds;
+      const int e = (it % kDgXcds) + kDgXcds * (slot / ntiles);
+      if (e >= E) continue;
+      const int r0 = dEoff[e], m = dEoff[e + 1] - r0;
+      if (m <= 0) continue;
+      p.e = __builtin_amdgcn_readfirstlane(e);
+      p.nt = __builtin_amdgcn_readfirstlane(slot % ntiles);
+      p.r0 = __builtin_amdgcn_readfirstlane(r0);
+      p.mb = 0;
+      p.rows = __builtin_amdgcn_readfirstlane(min(kDgRows, m));
+      return true;
+    }
+    return false;
+  };
+  auto next_pass = [&](int& it, const DPass& c, DPass& p) __attribute__((always_inline)) {
+    const int m = dEoff[c.e + 1] - c.r0;
+    if (c.mb + kDgRows < m) {
+      p = c;
+      p.mb = c.mb + kDgRows;
+      p.rows = __builtin_amdgcn_readfirstlane(min(kDgRows, m - p.mb));
+      return true;
+    }
+    it += grid;
+    return first_pass(it, p);
+  };
+  // A copies of this wave for a pass: instruction q fills pass rows
+  // 16 (2 wave + q) + lane / 4, only blocks of 16 that hold pass rows (later
+  // rows repeat the last one)
+  auto a_src = [&](const DPass& p, uint32_t (&aoff)[2]) __attribute__((always_inline)) {
     int nca = 0;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int row = 16 * (2 * wave + q) + lane / 4;
-      if (16 * (2 * wave + q) < rows) ++nca;
-      aoff[q] = (uint32_t)((r0 + mb + min(row, rows - 1)) * I + 8 * dg_pos(row, lane % 4)) * 2u;
+      if (16 * (2 * wave + q) < p.rows) ++nca;
+      aoff[q] = (uint32_t)((p.r0 + p.mb + min(row, p.rows - 1)) * I + 8 * dg_pos(row, lane % 4)) * 2u;
     }
-    nca = __builtin_amdgcn_readfirstlane(nca);
-    const int dmas = nca + 2;
+    return __builtin_amdgcn_readfirstlane(nca);
+  };
+  // stage hh of a pass into the slot of global stage g; returns this wave's copies
+  auto issue = [&](const DPass& p, const uint32_t (&aoff)[2], int nca, int hh, int g)
+      __attribute__((always_inline)) {
+    const uint32_t sl = ring + (uint32_t)((g % kDgSlots) * kDgSlotBytes);
+    const uint32_t koff = (uint32_t)hh * (kDgStageK * 2);
+    const uint16_t* wbase = w + ((size_t)p.e * H + (size_t)p.nt * kDgCols) * I;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (q < nca) dg_dma16(aoff[q] + koff, a16, sl + (2 * wave + q) * 1024);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) dg_dma16(boff[q] + koff, wbase, sl + kDgASlot + (2 * wave + q) * 1024);
+    return nca + 2;
+  };
 
-    auto issue = [&](int h) __attribute__((always_inline)) {
-      const uint32_t sl = ring + (uint32_t)((h % kDgSlots) * kDgSlotBytes);
-      const uint32_t koff = (uint32_t)h * (kDgStageK * 2);
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-        if (q < nca) dg_dma16(aoff[q] + koff, a16, sl + (2 * wave + q) * 1024);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) dg_dma16(boff[q] + koff, wbase, sl + kDgASlot + (2 * wave + q) * 1024);
-    };
-    // this wave's copies of stage h are in LDS: the (up to two) stages issued
-    // after it may stay in flight
-    auto wait_stage = [&](int h) __attribute__((always_inline)) {
-      const int ahead = min(S - 1 - h, kDgSlots - 2);
-      const int later = ahead * dmas;
-      if (later == 8) __builtin_amdgcn_s_waitcnt(dg_vm(8));
-      else if (later == 6) __builtin_amdgcn_s_waitcnt(dg_vm(6));
-      else if (later == 4) __builtin_amdgcn_s_waitcnt(dg_vm(4));
-      else if (later == 3) __builtin_amdgcn_s_waitcnt(dg_vm(3));
-      else if (later == 2) __builtin_amdgcn_s_waitcnt(dg_vm(2));
-      else __builtin_amdgcn_s_waitcnt(dg_vm(0));
-    };
+  int item = blockIdx.x;
+  DPass cur;
+  if (!first_pass(item, cur)) return;
+  uint32_t ca[2];
+  int cn = a_src(cur, ca);
+  // copies in flight are those of the stage waited for next and of the two
+  // after it; c2 and c3 count the latter two
+  issue(cur, ca, cn, 0, 0);
+  int c2 = issue(cur, ca, cn, 1, 1), c3 = issue(cur, ca, cn, 2, 2);
+  int g0 = 0;                   // global stage of the current pass's stage 0
+  bool prewaited = false;
+
+  while (true) {
+    DPass nx;
+    int item_n = item;
+    const bool has_next = next_pass(item_n, cur, nx);
+    uint32_t na_off[2] = {0u, 0u};
+    int nn = 0;
+    if (has_next) nn = a_src(nx, na_off);
+    const int mtiles = (cur.rows + 31) / 32;
+    const int na = (mtiles - wm + 1) / 2;     // live m-tiles 2a + wm of this wave
 
     auto run = [&](auto na_c) __attribute__((always_inline)) {
       constexpr int NA = decltype(na_c)::value;
@@ -250,14 +315,21 @@ k_down_gemm(const uint16_t* __restrict__ a16, int I, const uint16_t* __restrict_
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int j = 0; j < 16; ++j) R[a][c][j] = 0.0f;
-      __builtin_amdgcn_s_barrier();  // nobody still reads the ring of the previous pass
-      for (int h = 0; h < kDgSlots - 1 && h < S; ++h) issue(h);
-      for (int h = 0; h < S; ++h) {
-        wait_stage(h);
-        __builtin_amdgcn_s_barrier();                       // ... and every other wave's
-        if (h + kDgSlots - 1 < S) issue(h + kDgSlots - 1);  // into the slot of stage h - 1, now free
+      for (int hh = 0; hh < S; ++hh) {
+        const int gs = g0 + hh;
+        // this wave's copies of stage gs are in LDS (those of the two stages
+        // after it may stay in flight), then every other wave's
+        if (!prewaited) dg_wait_rt(c2 + c3);
+        prewaited = false;
+        __builtin_amdgcn_s_barrier();
+        // into the slot of stage gs - 1, now free: stage hh + 3 of this pass, or of the next
+        int c = 0;
+        if (hh + 3 < S) c = issue(cur, ca, cn, hh + 3, gs + 3);
+        else if (has_next) c = issue(nx, na_off, nn, hh + 3 - S, gs + 3);
+        c2 = c3;
+        c3 = c;
         if constexpr (NA > 0) {
-          const uint8_t* sl = dRing + (h % kDgSlots) * kDgSlotBytes;
+          const uint8_t* sl = dRing + (gs % kDgSlots) * kDgSlotBytes;
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
             const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(sl + boffs[s][0]);
@@ -271,10 +343,16 @@ k_down_gemm(const uint16_t* __restrict__ a16, int I, const uint16_t* __restrict_
           }
         }
       }
+      // wait now for the next pass's first stage: the stores below also count in
+      // vmcnt and may complete in any order relative to the copies
+      if (has_next) {
+        dg_wait_rt(c2 + c3);
+        prewaited = true;
+      }
       if constexpr (NA > 0) {
         // a uniform base and 32-bit lane offsets, made opaque per tile so the
         // compiler does not hoist every store address of the pass at once
-        float* yb = y + (size_t)(r0 + mb) * H + (size_t)nt * kDgCols + 64 * wn;
+        float* yb = y + (size_t)(cur.r0 + cur.mb) * H + (size_t)cur.nt * kDgCols + 64 * wn;
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
           uint32_t o = (uint32_t)((32 * (2 * a + wm) + 4 * half) * H + col);
@@ -284,7 +362,7 @@ k_down_gemm(const uint16_t* __restrict__ a16, int I, const uint16_t* __restrict_
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
               const int dr = 8 * (j / 4) + (j % 4);
-              if (32 * (2 * a + wm) + 4 * half + dr < rows) yb[o + (uint32_t)(dr * H + 32 * c)] = R[a][c][j];
+              if (32 * (2 * a + wm) + 4 * half + dr < cur.rows) yb[o + (uint32_t)(dr * H + 32 * c)] = R[a][c][j];
             }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -297,6 +375,13 @@ k_down_gemm(const uint16_t* __restrict__ a16, int I, const uint16_t* __restrict_
       case 3: run(std::integral_constant<int, 3>{}); break;
       default: run(std::integral_constant<int, 4>{}); break;
     }
+    if (!has_next) break;
+    cur = nx;
+    ca[0] = na_off[0];
+    ca[1] = na_off[1];
+    cn = nn;
+    item = item_n;
+    g0 += S;
   }
 }
 
@@ -341,7 +426,7 @@ hipError_t launch_down_gemm_combine(const float* act, int T, int I, const uint16
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int ntiles = H / kDgCols;
-  const int grid = cdiv(E, kDgXcds) * kDgXcds * ntiles;
+  const int grid = min(cdiv(E, kDgXcds) * kDgXcds * ntiles, kDgBlocks);   // both multiples of 8
   k_down_gemm<<<grid, kDgThreads, 0, st>>>(a16, I, w, E, H, expert_off, y, ntiles);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
