@@ -155,7 +155,7 @@ def main():
                                             act=act, out=b)
         elif fp8:
             i8h.moe_gateup_fp8blk_grouped(xs[i % nb], codes[c], scales[c], k, b["expert_off"], b["sorted_pairs"],
-                                          gate_up=False, act=act, workspace=fp8_ws)
+                                          gate_up=False, act=act, workspace=fp8_ws, path=args.path)
         elif fused:
             i8h.moe_gateup_i8h_grouped_fused(xs[i % nb], codes[c], scales[c], k, b["expert_off"],
                                              b["sorted_pairs"], gate_up=False, act=act)
@@ -239,8 +239,10 @@ def main():
     flops = 2.0 * L.P * L.N * L.K
     if one_launch:
         kernel_name, key = "k_route_gateup_decode (routing + rotation + gate_up)", "route_gateup_decode"
-    elif fp8:
+    elif fp8 and (args.path == "gemm" or (args.path == "auto" and L.P >= 32 * L.E)):
         kernel_name, key = "k_gateup_gemm<E4M3> (+ k_fp8_act_quant)", "gemm_e4m3"
+    elif fp8:
+        kernel_name, key = "k_gateup_fp8_skinny (+ k_fp8_act_quant)", "skinny_e4m3"
     elif args.path == "gemv" or (args.path == "auto" and L.T <= 8):
         kernel_name = "k_gateup_i8h_gemv" + ("<rotation fused>" if fused else "")
         key = "gemv_rot" if fused else "gemv"
@@ -302,6 +304,7 @@ KERNEL_SOURCES = {
     "down_gemm": ["down.hip", "xlane.hpp", "common.hpp"],
     "linear": ["linear.hip", "common.hpp"],
     "skinny": ["gateup_skinny.hip", "common.hpp"],
+    "skinny_e4m3": ["gateup_skinny.hip", "gateup_fp8.hip", "common.hpp"],
 }
 
 

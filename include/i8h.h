@@ -219,6 +219,22 @@ int moe_gateup_fp8blk_grouped(const uint16_t* x, int T, int K,
                               float* gate_up, float* act,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* Same as moe_gateup_fp8blk_grouped with the kernel chosen by the caller:
+ * I8H_PATH_AUTO (as the call above: GEMM when the pairs average at least 32
+ * per expert, else SKINNY), I8H_PATH_GEMM (bf16 MFMA, passes of 128 pairs,
+ * units of 128 gate + 128 up columns) or I8H_PATH_SKINNY (bf16 MFMA for few
+ * pairs per expert: passes of 64 pairs, units of 64 gate + 64 up columns,
+ * several workgroups per CU). Both give the same result to float32 rounding
+ * order. I8H_PATH_GEMV and I8H_PATH_TALL have no E4M3 form:
+ * I8H_EUNSUPPORTED; any other value: I8H_EINVAL. */
+int moe_gateup_fp8blk_grouped_path(const uint16_t* x, int T, int K,
+                                   const uint8_t* codes, const uint16_t* scales,
+                                   int E, int N, int topk,
+                                   const int32_t* expert_off, const int32_t* sorted_pairs,
+                                   float* gate_up, float* act,
+                                   void* workspace, size_t workspace_bytes, int path,
+                                   void* stream);
+
 /* ------------------------------------------------------------------------
  * The step after the path: bf16 grouped down projection of the routed
  * experts, then the weighted combine of each token's topk outputs.

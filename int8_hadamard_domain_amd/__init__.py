@@ -65,6 +65,7 @@ def lib():
         "fp8_quantize_activations": (I, [P, I, I, P, P, P]),
         "moe_gateup_fp8blk_workspace_size": (SZ, [I, I]),
         "moe_gateup_fp8blk_grouped": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P, SZ, P]),
+        "moe_gateup_fp8blk_grouped_path": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P, SZ, I, P]),
         "moe_down_bf16_workspace_size": (SZ, [I, I, I, I]),
         "moe_down_bf16_combine": (I, [P, I, I, P, I, I, I, P, P, P, P, P, P, SZ, P]),
         "moe_down_bf16_combine_path": (I, [P, I, I, P, I, I, I, P, P, P, P, P, P, SZ, I, P]),
@@ -252,12 +253,13 @@ def fp8_quantize_activations(x, qx=None, sx=None):
 
 
 def moe_gateup_fp8blk_grouped(x, codes, scales, topk, expert_off, sorted_pairs,
-                              gate_up=True, act=True, workspace=None):
+                              gate_up=True, act=True, workspace=None, path="auto"):
     """Grouped FP8 E4M3 128x128-block gate_up.
 
     x [T, K] bf16 (not rotated), codes [E, N, K] uint8 (E4M3 bytes), scales
-    [E, N/128, K/128] bf16. Returns (gate_up, act, workspace); the workspace
-    holds the quantized activations (see fp8_workspace_views).
+    [E, N/128, K/128] bf16. path: "auto", "gemm" or "skinny". Returns
+    (gate_up, act, workspace); the workspace holds the quantized activations
+    (see fp8_workspace_views).
     """
     _dev(x, "x", torch.bfloat16, 2)
     _dev(codes, "codes", torch.uint8, 3)
@@ -275,9 +277,9 @@ def moe_gateup_fp8blk_grouped(x, codes, scales, topk, expert_off, sorted_pairs,
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     gu = _out(gate_up, (T * topk, N), dev)
     ac = _out(act, (T * topk, N // 2), dev)
-    _check("moe_gateup_fp8blk_grouped", lib().moe_gateup_fp8blk_grouped(
+    _check("moe_gateup_fp8blk_grouped", lib().moe_gateup_fp8blk_grouped_path(
         _ptr(x), T, K, _ptr(codes), _ptr(scales), E, N, topk, _ptr(expert_off), _ptr(sorted_pairs),
-        _ptr(gu), _ptr(ac), _ptr(workspace), workspace.numel(), _stream(dev)))
+        _ptr(gu), _ptr(ac), _ptr(workspace), workspace.numel(), PATHS[path], _stream(dev)))
     return gu, ac, workspace
 
 

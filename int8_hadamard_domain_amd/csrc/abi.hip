@@ -278,13 +278,15 @@ int moe_route_gateup_i8h_decode(const float* logits, const uint16_t* x, int T, i
                                                   as_stream(stream)));
 }
 
-int moe_gateup_fp8blk_grouped(const uint16_t* x, int T, int K, const uint8_t* codes, const uint16_t* scales, int E,
-                              int N, int topk, const int32_t* expert_off, const int32_t* sorted_pairs,
-                              float* gate_up, float* act, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+int moe_gateup_fp8blk_grouped_path(const uint16_t* x, int T, int K, const uint8_t* codes, const uint16_t* scales,
+                                   int E, int N, int topk, const int32_t* expert_off, const int32_t* sorted_pairs,
+                                   float* gate_up, float* act, void* workspace, size_t workspace_bytes, int path,
+                                   void* stream) {
   int rc = check_common_moe(T, K, E, N, topk);
   if (rc != I8H_OK) return rc;
   if ((N % 128) != 0) return I8H_EINVAL;
+  if (path < I8H_PATH_AUTO || path > I8H_PATH_SKINNY) return I8H_EINVAL;
+  if (path == I8H_PATH_GEMV || path == I8H_PATH_TALL) return I8H_EUNSUPPORTED;
   if (T == 0) return I8H_OK;
   if (!x || !codes || !scales || !expert_off || !sorted_pairs) return I8H_EINVAL;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(expert_off, 4) ||
@@ -294,14 +296,30 @@ int moe_gateup_fp8blk_grouped(const uint16_t* x, int T, int K, const uint8_t* co
   size_t need = moe_gateup_fp8blk_workspace_size(T, K);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return I8H_EINVAL;
   if (!gate_up && !act) return I8H_OK;
+  // as for int8: 128-pair passes once experts average 32 pairs, below that
+  // the small-unit kernel
+  if (path == I8H_PATH_AUTO)
+    path = (int64_t)T * topk >= (int64_t)32 * E ? I8H_PATH_GEMM : I8H_PATH_SKINNY;
   Fp8Ws lay(T, K);
   uint8_t* qx = static_cast<uint8_t*>(workspace);
   float* sx = reinterpret_cast<float*>(qx + lay.sx_off);
   uint16_t* xq = reinterpret_cast<uint16_t*>(qx + lay.xq_off);
-  hipError_t e = i8h::launch_fp8_act_quant(x, T, K, qx, sx, xq, as_stream(stream));
+  hipStream_t st = as_stream(stream);
+  hipError_t e = i8h::launch_fp8_act_quant(x, T, K, qx, sx, xq, st);
   if (e != hipSuccess) return I8H_EHIP;
+  if (path == I8H_PATH_SKINNY)
+    return from_hip(i8h::launch_gateup_fp8_skinny(xq, sx, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs,
+                                                  gate_up, act, st));
   return from_hip(i8h::launch_gateup_fp8(xq, sx, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs,
-                                         gate_up, act, as_stream(stream)));
+                                         gate_up, act, st));
+}
+
+int moe_gateup_fp8blk_grouped(const uint16_t* x, int T, int K, const uint8_t* codes, const uint16_t* scales, int E,
+                              int N, int topk, const int32_t* expert_off, const int32_t* sorted_pairs,
+                              float* gate_up, float* act, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return moe_gateup_fp8blk_grouped_path(x, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up, act,
+                                        workspace, workspace_bytes, I8H_PATH_AUTO, stream);
 }
 
 // bf16 grouped down projection + weighted combine

@@ -1,10 +1,14 @@
-// Grouped int8 Hadamard-domain gate_up for few pairs per expert (a verify
-// batch: 128 tokens x top-8 over 128 experts is about 8 pairs an expert).
+// Grouped gate_up for few pairs per expert (a verify batch: 128 tokens x
+// top-8 over 128 experts is about 8 pairs an expert), for both weight formats.
 //
-// Format (int8 card, model table row "Weights"): int8 codes -127..127, one
-// bf16 scale per row and 128 of K, activations rotated bf16.
+// int8 Hadamard-domain (int8 card, model table row "Weights"): int8 codes
+// -127..127, one bf16 scale per row and 128 of K, activations rotated bf16.
 //   gu[r, n] = sum_g s[e, n, g] * sum_{kk in g} q[e, n, kk] * x_rot[t, kk]
-//   act[r, i] = gelu_tanh(gu[r, i]) * gu[r, I + i]
+// FP8 E4M3 128x128 blocks (FP8 card, model table row "Weights"): one bf16
+// scale per block, activations quantized per token and 128 of K (float32
+// factor sx, E4M3 codes handed over as their exact bf16 values).
+//   gu[r, n] = sum_g (sw[e, n/128, g] * sx[t, g]) * sum_{kk in g} qw * qx
+// Both: act[r, i] = gelu_tanh(gu[r, i]) * gu[r, I + i].
 //
 // With a handful of pairs per expert the step is a stream of the touched
 // experts' codes, and what bounds it is how many bytes each CU keeps in
@@ -13,12 +17,13 @@
 // streams): unit = expert e x (64 gate + the matching 64 up columns) x passes
 // of 64 pairs; 4 waves, wave w takes gate columns 32 (w & 1) .. +31 and the
 // matching up columns for the m-tile w >> 1 (32 pass rows). K goes in stages
-// of 64 through a 3-slot LDS ring (A 8 KB, B 8 KB, scales 512 B a slot: 49.5
-// KB a workgroup, so three share a CU) by gfx950's global -> LDS DMA, two
-// stages ahead. Each 128-K
-// group's products accumulate from zero and are folded into the float32
-// result with the group's scale; v_mfma_f32_32x32x16_bf16 on codes decoded to
-// bf16 exactly.
+// of 64 through a 3-slot LDS ring (A 8 KB, B 8 KB, side data 512 B a slot:
+// 49.5 KB a workgroup, so three share a CU) by gfx950's global -> LDS DMA,
+// two stages ahead. Each 128-K group's products accumulate from zero and are
+// folded into the float32 result with the group's scale (int8: the column's;
+// E4M3: block scale times the pass row's sx); v_mfma_f32_32x32x16_bf16 on
+// codes decoded to bf16 exactly (int8 by byte converts, E4M3 by
+// v_cvt_pk_f32_fp8: both fit bf16's significand).
 //
 // Stage layouts as in the larger kernels: A piece p (8 bf16) of row r (128
 // bytes) at p ^ ((r >> 1) & 7), B piece p (16 codes) of row r (64 bytes) at
@@ -47,8 +52,10 @@ __shared__ __attribute__((aligned(16))) uint16_t sA2[kSRows * kSStageK];
 __shared__ __attribute__((aligned(16))) uint8_t sB0[2 * kSGate * kSStageK];
 __shared__ __attribute__((aligned(16))) uint8_t sB1[2 * kSGate * kSStageK];
 __shared__ __attribute__((aligned(16))) uint8_t sB2[2 * kSGate * kSStageK];
-// the dword holding the bf16 scale of each of the unit's 128 code rows, for
-// the group whose second stage this slot holds (second stages land in any slot)
+// side data of the group whose second stage this slot holds (second stages
+// land in any slot): int8 -> the dword holding the bf16 scale of each of the
+// unit's 128 code rows; E4M3 -> the sx of the 64 pass rows, then 64 dwords
+// holding the gate (even lanes) and up (odd lanes) block scales
 __shared__ __attribute__((aligned(16))) uint32_t sC0[2 * kSGate];
 __shared__ __attribute__((aligned(16))) uint32_t sC1[2 * kSGate];
 __shared__ __attribute__((aligned(16))) uint32_t sC2[2 * kSGate];
@@ -86,20 +93,36 @@ __device__ __forceinline__ void s_wait_dyn(int n) {
 __device__ __forceinline__ int sa_pos(int row, int piece) { return piece ^ ((row >> 1) & 7); }
 __device__ __forceinline__ int sb_pos(int row, int piece) { return piece ^ ((row >> 2) & 3); }
 
+enum class SFmt { I8, E4M3 };
+
+template <SFmt F>
 __device__ __forceinline__ bf16x8 s_decode(uint32_t lo, uint32_t hi) {
   u32x4 p;
-  p[0] = pack_bf16x2(sbyte<0>(lo), sbyte<1>(lo));
-  p[1] = pack_bf16x2(sbyte<2>(lo), sbyte<3>(lo));
-  p[2] = pack_bf16x2(sbyte<0>(hi), sbyte<1>(hi));
-  p[3] = pack_bf16x2(sbyte<2>(hi), sbyte<3>(hi));
+  if constexpr (F == SFmt::I8) {
+    p[0] = pack_bf16x2(sbyte<0>(lo), sbyte<1>(lo));
+    p[1] = pack_bf16x2(sbyte<2>(lo), sbyte<3>(lo));
+    p[2] = pack_bf16x2(sbyte<0>(hi), sbyte<1>(hi));
+    p[3] = pack_bf16x2(sbyte<2>(hi), sbyte<3>(hi));
+  } else {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+    const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+    const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+    const f2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+    p[0] = pack_bf16x2(a[0], a[1]);
+    p[1] = pack_bf16x2(b[0], b[1]);
+    p[2] = pack_bf16x2(c[0], c[1]);
+    p[3] = pack_bf16x2(d[0], d[1]);
+  }
   return __builtin_bit_cast(bf16x8, p);
 }
 
-__global__ void __launch_bounds__(kSThreads, 3)
-k_gateup_i8h_skinny(const uint16_t* __restrict__ xa, int K, const uint8_t* __restrict__ codes,
-                    const uint16_t* __restrict__ scales, int E, int N, int k,
-                    const int32_t* __restrict__ expert_off, const int32_t* __restrict__ sorted_pairs,
-                    float* __restrict__ gu, float* __restrict__ act, int ntiles) {
+template <SFmt F>
+__device__ __forceinline__ void skinny_body(const uint16_t* __restrict__ xa, const float* __restrict__ sx, int K,
+                                            const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+                                            int E, int N, int k, const int32_t* __restrict__ expert_off,
+                                            const int32_t* __restrict__ sorted_pairs, float* __restrict__ gu,
+                                            float* __restrict__ act, int ntiles) {
   // the units of expert e run on XCD e % 8, consecutive in dispatch order
   const int blk = blockIdx.x;
   const int slot = blk / kSXcds;
@@ -110,7 +133,7 @@ k_gateup_i8h_skinny(const uint16_t* __restrict__ xa, int K, const uint8_t* __res
   const int m_e = expert_off[e + 1] - r0;
   if (m_e <= 0) return;
 
-  const int I = N / 2, G = K / kGroup;
+  const int I = N / 2, G = K / kGroup, NB = N / kGroup;
   const int S = 2 * G;                            // stages per pass
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -133,17 +156,31 @@ k_gateup_i8h_skinny(const uint16_t* __restrict__ xa, int K, const uint8_t* __res
     const int n = gi < I ? (row < kSGate ? gi : I + gi) : 0;
     bsrc[q] = ((size_t)e * N + n) * K + 16 * sb_pos(row, lane % 4);
   }
-  // waves 0, 1 copy the scale dword of code row 64 wave + lane with the second
-  // stage of each group (element index cbase + g; the bf16 is its half (cbase + g) & 1)
+  // side data copied with the second stage of group g (dword of element
+  // index cbase + g; the wanted bf16 is its half (cbase + g) & 1):
+  //   int8, waves 0, 1: the scale of code row 64 wave + lane
+  //   E4M3, wave 0: sx of pass row lane (set per pass); wave 1: the gate
+  //   (even lanes) or up (odd lanes) block scale of the unit's 64 columns,
+  //   which lie in one 128-column block each
   int64_t cbase = 0;
-  {
+  if constexpr (F == SFmt::I8) {
     const int row = 64 * (wave & 1) + lane;
     const int gi = nt * kSGate + (row % kSGate);
     const int n = gi < I ? (row < kSGate ? gi : I + gi) : 0;
     cbase = ((int64_t)e * N + n) * G;
+  } else {
+    const int gi = nt * kSGate;                   // < I for every launched tile
+    const int nb = (lane & 1) ? (I + gi) / kGroup : gi / kGroup;
+    cbase = ((int64_t)e * NB + nb) * G;
   }
-  const int par_g = (int)((((int64_t)e * N + (live ? i0 + col : 0)) * G) & 1);
-  const int par_u = (int)((((int64_t)e * N + (live ? I + i0 + col : 0)) * G) & 1);
+  int par_g, par_u;
+  if constexpr (F == SFmt::I8) {
+    par_g = (int)((((int64_t)e * N + (live ? i0 + col : 0)) * G) & 1);
+    par_u = (int)((((int64_t)e * N + (live ? I + i0 + col : 0)) * G) & 1);
+  } else {
+    par_g = (int)((((int64_t)e * NB + (nt * kSGate) / kGroup) * G) & 1);
+    par_u = (int)((((int64_t)e * NB + (I + nt * kSGate) / kGroup) * G) & 1);
+  }
 
   for (int mb = 0; mb < m_e; mb += kSRows) {
     const int rows = min(kSRows, m_e - mb);
@@ -161,6 +198,8 @@ k_gateup_i8h_skinny(const uint16_t* __restrict__ xa, int K, const uint8_t* __res
       if (8 * (2 * wave + q) < rows) ++nca;
     }
     nca = __builtin_amdgcn_readfirstlane(nca);
+    int xtok = 0;                                 // E4M3, wave 0: token of pass row lane
+    if constexpr (F == SFmt::E4M3) xtok = sorted_pairs[r0 + mb + min(lane, rows - 1)] / k;
     // copies of stage h by this wave
     auto dmas = [&](int h) { return nca + 2 + ((wave < 2 && (h & 1)) ? 1 : 0); };
     // stage h into ring slot sl (== h % 3, given as a constant by the caller)
@@ -171,8 +210,12 @@ k_gateup_i8h_skinny(const uint16_t* __restrict__ xa, int K, const uint8_t* __res
         if (q < nca) s_dma16(xa + asrc[q] + koff, la[sl] + (2 * wave + q) * (8 * kSStageK * 2));
 #pragma unroll
       for (int q = 0; q < 2; ++q) s_dma16(codes + bsrc[q] + koff, lb[sl] + (2 * wave + q) * (16 * kSStageK));
-      if ((h & 1) && wave < 2)
-        s_dma4(scales + ((cbase + h / 2) & ~(int64_t)1), lc[sl] + 64 * 4 * wave);
+      if ((h & 1) && wave < 2) {
+        if (F == SFmt::E4M3 && wave == 0)
+          s_dma4(sx + (size_t)xtok * G + h / 2, lc[sl]);
+        else
+          s_dma4(scales + ((cbase + h / 2) & ~(int64_t)1), lc[sl] + 64 * 4 * wave);
+      }
     };
 
     f32x16 acc[2], tmp[2];
@@ -202,17 +245,32 @@ k_gateup_i8h_skinny(const uint16_t* __restrict__ xa, int K, const uint8_t* __res
         const u32x2 cuw = *reinterpret_cast<const u32x2*>(&bbuf[ru * kSStageK + 16 * sb_pos(ru, s) + 8 * half]);
         const int m = mw + col;
         const bf16x8 av = *reinterpret_cast<const bf16x8*>(&abuf[m * kSStageK + 8 * sa_pos(m, 2 * s + half)]);
-        tmp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, s_decode(cgw[0], cgw[1]), tmp[0], 0, 0, 0);
-        tmp[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, s_decode(cuw[0], cuw[1]), tmp[1], 0, 0, 0);
+        tmp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, s_decode<F>(cgw[0], cgw[1]), tmp[0], 0, 0, 0);
+        tmp[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, s_decode<F>(cuw[0], cuw[1]), tmp[1], 0, 0, 0);
       }
       if (h & 1) {
         const int g = h / 2;
-        const float sg = __uint_as_float(((par_g + g) & 1) ? (cbuf[rg] & 0xffff0000u) : (cbuf[rg] << 16));
-        const float su = __uint_as_float(((par_u + g) & 1) ? (cbuf[ru] & 0xffff0000u) : (cbuf[ru] << 16));
+        auto half_bf16 = [](uint32_t w, int odd) { return __uint_as_float(odd ? (w & 0xffff0000u) : (w << 16)); };
+        if constexpr (F == SFmt::I8) {
+          const float sg = half_bf16(cbuf[rg], (par_g + g) & 1), su = half_bf16(cbuf[ru], (par_u + g) & 1);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          acc[0][j] = fmaf(tmp[0][j], sg, acc[0][j]);
-          acc[1][j] = fmaf(tmp[1][j], su, acc[1][j]);
+          for (int j = 0; j < 16; ++j) {
+            acc[0][j] = fmaf(tmp[0][j], sg, acc[0][j]);
+            acc[1][j] = fmaf(tmp[1][j], su, acc[1][j]);
+          }
+        } else {
+          const float wg = half_bf16(cbuf[kSRows], (par_g + g) & 1);
+          const float wu = half_bf16(cbuf[kSRows + 1], (par_u + g) & 1);
+          // sx of the lane's result rows mw + 4 half + 8 (j / 4) + j % 4
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 f = *reinterpret_cast<const f32x4*>(&cbuf[mw + 4 * half + 8 * q]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              acc[0][4 * q + i] = fmaf(tmp[0][4 * q + i], wg * f[i], acc[0][4 * q + i]);
+              acc[1][4 * q + i] = fmaf(tmp[1][4 * q + i], wu * f[i], acc[1][4 * q + i]);
+            }
+          }
         }
       }
     };
@@ -248,6 +306,22 @@ k_gateup_i8h_skinny(const uint16_t* __restrict__ xa, int K, const uint8_t* __res
   }
 }
 
+__global__ void __launch_bounds__(kSThreads, 3)
+k_gateup_i8h_skinny(const uint16_t* __restrict__ xa, int K, const uint8_t* __restrict__ codes,
+                    const uint16_t* __restrict__ scales, int E, int N, int k,
+                    const int32_t* __restrict__ expert_off, const int32_t* __restrict__ sorted_pairs,
+                    float* __restrict__ gu, float* __restrict__ act, int ntiles) {
+  skinny_body<SFmt::I8>(xa, nullptr, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu, act, ntiles);
+}
+
+__global__ void __launch_bounds__(kSThreads, 3)
+k_gateup_fp8_skinny(const uint16_t* __restrict__ xq, const float* __restrict__ sx, int K,
+                    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int E, int N, int k,
+                    const int32_t* __restrict__ expert_off, const int32_t* __restrict__ sorted_pairs,
+                    float* __restrict__ gu, float* __restrict__ act, int ntiles) {
+  skinny_body<SFmt::E4M3>(xq, sx, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu, act, ntiles);
+}
+
 }  // namespace
 
 hipError_t launch_gateup_i8h_skinny(const uint16_t* xrot, int T, int K, const int8_t* codes,
@@ -258,6 +332,17 @@ hipError_t launch_gateup_i8h_skinny(const uint16_t* xrot, int T, int K, const in
   const int grid = cdiv(E, kSXcds) * kSXcds * ntiles;
   k_gateup_i8h_skinny<<<grid, kSThreads, 0, st>>>(xrot, K, reinterpret_cast<const uint8_t*>(codes), scales, E, N,
                                                   k, expert_off, sorted_pairs, gu, act, ntiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup_fp8_skinny(const uint16_t* xq, const float* sx, int T, int K, const uint8_t* codes,
+                                    const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
+                                    const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st) {
+  (void)T;
+  const int ntiles = cdiv(N / 2, kSGate);
+  const int grid = cdiv(E, kSXcds) * kSXcds * ntiles;
+  k_gateup_fp8_skinny<<<grid, kSThreads, 0, st>>>(xq, sx, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu,
+                                                  act, ntiles);
   return hipGetLastError();
 }
 

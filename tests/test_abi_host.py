@@ -33,7 +33,7 @@ def L():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -132,6 +132,13 @@ def test_fp8_validation(L):
     assert f(A, 4, 256, A, A, 8, 256, 2, A, A, A, A, A, 16, None) == EINVAL         # too small
     assert f(A, 4, 256, A, A, 8, 256, 2, A, A, A, A, ctypes.c_void_p(0x10010), 1 << 20, None) == EINVAL
     assert f(A, 0, 256, A, A, 8, 256, 2, A, A, A, A, None, 0, None) == OK
+    fp = L.moe_gateup_fp8blk_grouped_path
+    assert fp(A, 4, 256, A, A, 8, 256, 2, A, A, A, A, A, 1 << 20, 5, None) == EINVAL    # no such path
+    assert fp(A, 4, 256, A, A, 8, 256, 2, A, A, A, A, A, 1 << 20, -1, None) == EINVAL
+    assert fp(A, 4, 256, A, A, 8, 256, 2, A, A, A, A, A, 1 << 20, 1, None) == EUNSUP    # GEMV: no E4M3 form
+    assert fp(A, 4, 256, A, A, 8, 256, 2, A, A, A, A, A, 1 << 20, 3, None) == EUNSUP    # TALL: no E4M3 form
+    assert fp(A, 4, 256, A, A, 8, 192, 2, A, A, A, A, A, 1 << 20, 4, None) == EINVAL    # N % 128
+    assert fp(A, 0, 256, A, A, 8, 256, 2, A, A, A, A, None, 0, 4, None) == OK
     q = L.fp8_quantize_activations
     assert q(A, 4, 100, A, A, None) == EINVAL
     assert q(ODD, 4, 128, A, A, None) == EINVAL

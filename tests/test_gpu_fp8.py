@@ -15,6 +15,8 @@ from tests.gpu_util import assert_close, bf16_cuda
 
 pytestmark = pytest.mark.gpu
 
+PATHS = ("gemm", "skinny", "auto")
+
 
 def _quant_compare(xb):
     print(f"fp8 act quant {xb.shape}", flush=True)
@@ -68,14 +70,15 @@ def _layer_fp8(L, experts_dense=True):
     return synth.synthetic_fp8(L)
 
 
-def _run(L, codes, sbits, rows=None, what=""):
+def _run(L, codes, sbits, rows=None, what="", path="auto"):
     lg = synth.router_logits(L)
     xb = synth.activations_bf16(L)
     r = router.route(lg, L.topk)
+    what = f"{what} {path}"
     print(f"fp8 gateup {what}", flush=True)
     gu, act, ws = i8h.moe_gateup_fp8blk_grouped(
         bf16_cuda(xb), torch.from_numpy(codes).cuda(), bf16_cuda(sbits), L.topk,
-        torch.from_numpy(r["expert_off"]).cuda(), torch.from_numpy(r["sorted_pairs"]).cuda())
+        torch.from_numpy(r["expert_off"]).cuda(), torch.from_numpy(r["sorted_pairs"]).cuda(), path=path)
     torch.cuda.synchronize()
     qx, sx = quant.quantize_fp8_activations(synth.bf16_bits_to_f64(xb))
     # the workspace keeps the quantized activations: bit-exact
@@ -91,19 +94,22 @@ def _run(L, codes, sbits, rows=None, what=""):
     assert_close(act.cpu().numpy()[sel], gateup.epilogue(ref), what + " act")
 
 
-def test_small_layer_oracle_quantized(gpu_available):
+@pytest.mark.parametrize("path", PATHS)
+def test_small_layer_oracle_quantized(gpu_available, path):
     L = synth.layer("fp8", T=6, K=256, E=4, topk=2, N=256)
     codes, sbits = _layer_fp8(L)
-    _run(L, codes, sbits, what="small")
+    _run(L, codes, sbits, what="small", path=path)
 
 
-def test_mid_layer_oracle_quantized(gpu_available):
+@pytest.mark.parametrize("path", PATHS)
+def test_mid_layer_oracle_quantized(gpu_available, path):
     L = synth.layer("fp8", T=70, E=4, topk=2)
     codes, sbits = _layer_fp8(L)
-    _run(L, codes, sbits, what="mid")
+    _run(L, codes, sbits, what="mid", path=path)
 
 
-def test_full_size_sampled(gpu_available):
+@pytest.mark.parametrize("path", PATHS)
+def test_full_size_sampled(gpu_available, path):
     L = synth.layer("fp8")
     codes, sbits = _layer_fp8(L, experts_dense=False)
     r = router.route(synth.router_logits(L), L.topk)
@@ -113,11 +119,12 @@ def test_full_size_sampled(gpu_available):
         if off[e + 1] > off[e]:
             rows.update([int(off[e]), int(off[e + 1] - 1)])
     rows.update(np.random.default_rng(4).integers(0, off[-1], 48).tolist())
-    _run(L, codes, sbits, rows=np.array(sorted(rows)), what="full")
+    _run(L, codes, sbits, rows=np.array(sorted(rows)), what="full", path=path)
 
 
-def test_ragged_and_large_m(gpu_available):
+@pytest.mark.parametrize("path", PATHS)
+def test_ragged_and_large_m(gpu_available, path):
     # one expert with 300 pairs (several m-passes), N = 128 (gate and up share a block)
     L = synth.layer("fp8", T=300, K=384, E=1, topk=1, N=128)
     codes, sbits = _layer_fp8(L)
-    _run(L, codes, sbits, what="ragged")
+    _run(L, codes, sbits, what="ragged", path=path)
