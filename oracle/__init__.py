@@ -15,7 +15,8 @@ Sources (the pages, by title):
     (the FP8 card): model table, row "Weights", and its recipe line.
   * "Gemma 4 12B-it · int8 · for radiance" and "Gemma 4 31B-it · int5 · for
     radiance": header table, row "Format" (per-token, per-128 activation
-    scales, the precedent for the FP8 activation quantizer).
+    scales, the precedent for the FP8 activation quantizer; the 12B card's
+    int8 weights + int8 activations are the W8A8 form of w8a8.py).
 
 Modules:
   numfmt   - bf16 and OCP E4M3FN codecs from their bit-level definitions
@@ -28,10 +29,12 @@ Modules:
              token's k expert outputs (the step after the path)
   dense    - the drafter's dense int8 linears with f16 scales (RTN, no
              transform) and their product
+  w8a8     - the int8 g128 W8A8 form: RTN weight and per-token activation
+             quantizers and the grouped gate_up on integer group sums
 
 Every function here is pinned by tests/test_oracle_*.py against closed
 forms, invariants, library special cases or brute force; none is marked
 "parity unpinned".
 """
 
-from . import numfmt, hadamard, quant, router, gateup, down, dense  # noqa: F401
+from . import numfmt, hadamard, quant, router, gateup, down, dense, w8a8  # noqa: F401
