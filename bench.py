@@ -6,7 +6,9 @@ expert gate_up layer (Gemma 4 26B-A4B shapes: hidden 2048, 128 experts,
 top-8, 2 x 768 gate_up rows per expert):
     moe_route_permute -> hadamard128_rotate -> moe_gateup_i8h_grouped (act out)
 For a few tokens the three run as one launch (moe_route_gateup_i8h_decode);
-for the FP8 block variant the step is moe_route_permute -> moe_gateup_fp8blk_grouped.
+for the FP8 block variant the step is moe_route_permute -> moe_gateup_fp8blk_grouped,
+for the W8A8 int8 g128 form (workload w8a8, prefill sizes) moe_route_permute ->
+moe_gateup_i8g_grouped.
 
 Default workload: one decode token (T = 1). Inputs are seeded synthetic data
 already resident in HBM; every step takes a different token (router logits
@@ -42,7 +44,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=512)
     ap.add_argument("--warmup", type=int, default=64)
-    ap.add_argument("--workload", default="decode", choices=["decode", "verify", "prefill", "fp8"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "verify", "prefill", "fp8", "w8a8"])
     ap.add_argument("--copies", type=int, default=0, help="weight copies cycled (0: enough to defeat caches)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -100,7 +102,8 @@ def main():
         bench_linear(args, dev)
         return
     fp8 = name == "fp8"
-    fused = (not fp8) and (not args.unfused) and args.path == "auto" and L.T <= 8
+    w8 = name == "w8a8"
+    fused = (not fp8) and (not w8) and (not args.unfused) and args.path == "auto" and L.T <= 8
     one_launch = fused and not args.two_launch and L.P <= 64 and L.E <= 256 and L.K <= 4096
     per_copy_bytes = L.E * L.N * L.K * (1 + (2 / (128 * 128) if fp8 else 2 / 128))
     if args.copies > 0:
@@ -146,6 +149,8 @@ def main():
     act = torch.empty((L.P, L.N // 2), dtype=torch.float32, device=dev)
     fp8_ws = torch.empty((max(i8h.lib().moe_gateup_fp8blk_workspace_size(L.T, L.K), 1),),
                          dtype=torch.uint8, device=dev)
+    i8g_ws = torch.empty((max(i8h.lib().moe_gateup_i8g_workspace_size(L.T, L.K), 1),),
+                         dtype=torch.uint8, device=dev)
 
     def gate_up(i):
         b = route_bufs[i]
@@ -156,6 +161,9 @@ def main():
         elif fp8:
             i8h.moe_gateup_fp8blk_grouped(xs[i % nb], codes[c], scales[c], k, b["expert_off"], b["sorted_pairs"],
                                           gate_up=False, act=act, workspace=fp8_ws, path=args.path)
+        elif w8:
+            i8h.moe_gateup_i8g_grouped(xs[i % nb], codes[c], scales[c], k, b["expert_off"], b["sorted_pairs"],
+                                       gate_up=False, act=act, workspace=i8g_ws)
         elif fused:
             i8h.moe_gateup_i8h_grouped_fused(xs[i % nb], codes[c], scales[c], k, b["expert_off"],
                                              b["sorted_pairs"], gate_up=False, act=act)
@@ -168,7 +176,7 @@ def main():
             gate_up(i)
             return
         i8h.moe_route_permute(logits[i % nb], k, out=route_bufs[i])
-        if not fp8 and not fused:
+        if not fp8 and not w8 and not fused:
             i8h.hadamard128_rotate(xs[i % nb], out=xr)
         gate_up(i)
 
@@ -233,12 +241,14 @@ def main():
     if one_launch:
         # the kernel also reads the logits and writes ids, weights and pair_pos
         alg_bytes += L.T * L.E * 4 + 3 * L.P * 4
-    if fp8:
+    if fp8 or w8:
         alg_bytes += L.T * L.K * 2 + L.T * L.G * 4       # quantizer reads bf16 x, writes scales
     achieved = alg_bytes / (kern_us * 1e-6) / 1e9
     flops = 2.0 * L.P * L.N * L.K
     if one_launch:
         kernel_name, key = "k_route_gateup_decode (routing + rotation + gate_up)", "route_gateup_decode"
+    elif w8:
+        kernel_name, key = "k_gateup_i8g (+ k_i8_act_quant)", "i8g"
     elif fp8 and (args.path == "gemm" or (args.path == "auto" and L.P >= 32 * L.E)):
         kernel_name, key = "k_gateup_gemm<E4M3> (+ k_fp8_act_quant)", "gemm_e4m3"
     elif fp8:
@@ -261,7 +271,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(L, nb, logits_np, x_np, codes_np, sbits_np, fp8, args.cpu_seconds, bytes_per_expert)
+        cpu = cpu_baseline(L, nb, logits_np, x_np, codes_np, sbits_np, "fp8" if fp8 else "i8g" if w8 else "i8h",
+                           args.cpu_seconds, bytes_per_expert)
 
     out = {
         "metric": METRIC,
@@ -275,7 +286,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3*fp8e4m3->f32" if fp8 else "i8*bf16->f32",
+        "dtype": "fp8e4m3*fp8e4m3->f32" if fp8 else "i8*i8->i32->f32" if w8 else "i8*bf16->f32",
         "data": "synthetic",
         "config": {"workload": f"{name}: T={L.T} K={L.K} E={L.E} top-{k} N={L.N} (gate_up of Gemma 4 26B-A4B)",
                    "T": L.T, "K": L.K, "E": L.E, "topk": k, "N": L.N, "weight_copies": int(copies),
@@ -283,6 +294,7 @@ def main():
                    "outputs": "act (fp32); gate_up not stored", "setup_s": round(setup_s, 1),
                    "step": ("route -> rotate -> gate_up in one launch" if one_launch else
                             "route -> gate_up (FP8 quantizer + product)" if fp8 else
+                            "route -> gate_up (int8 activation quantizer + int8 product)" if w8 else
                             "route -> gate_up with the rotation fused" if fused else
                             "route -> rotate -> gate_up")},
         "roofline": roofline,
@@ -305,6 +317,7 @@ KERNEL_SOURCES = {
     "linear": ["linear.hip", "common.hpp"],
     "skinny": ["gateup_skinny.hip", "common.hpp"],
     "skinny_e4m3": ["gateup_skinny.hip", "gateup_fp8.hip", "common.hpp"],
+    "i8g": ["gateup_i8g.hip", "xlane.hpp", "common.hpp"],
 }
 
 
@@ -553,9 +566,9 @@ def bench_linear(args, dev):
     }))
 
 
-def cpu_baseline(L, nb, logits_np, x_np, codes_np, sbits_np, fp8, budget_s, bytes_per_expert):
+def cpu_baseline(L, nb, logits_np, x_np, codes_np, sbits_np, fmt, budget_s, bytes_per_expert):
     """The fp64 oracle, as it stands, on the same steps until the budget is spent."""
-    from oracle import gateup, hadamard, numfmt, quant, router
+    from oracle import gateup, hadamard, numfmt, quant, router, w8a8
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
@@ -569,9 +582,12 @@ def cpu_baseline(L, nb, logits_np, x_np, codes_np, sbits_np, fp8, budget_s, byte
         lg = logits_np[done]
         x = numfmt.bf16_from_bits(x_np[done])
         r = router.route(lg, L.topk)
-        if fp8:
+        if fmt == "fp8":
             qx, sx = quant.quantize_fp8_activations(x)
             gu = gateup.gateup_fp8blk(qx, sx, codes_np, scales, r["expert_off"], r["sorted_pairs"], L.topk)
+        elif fmt == "i8g":
+            qx, sx = w8a8.quantize_i8_activations(x)
+            gu = w8a8.gateup_i8g(qx, sx, codes_np, scales, r["expert_off"], r["sorted_pairs"], L.topk)
         else:
             xr = hadamard.rotate_activations_bf16(x)
             gu = gateup.gateup_i8h(xr, codes_np, scales, r["expert_off"], r["sorted_pairs"], L.topk)
@@ -582,7 +598,8 @@ def cpu_baseline(L, nb, logits_np, x_np, codes_np, sbits_np, fp8, budget_s, byte
     el = time.perf_counter() - t0
     return {"value": round(wbytes / el / 1e9, 4), "unit": "GB/s", "tokens_per_s": round(tokens / el, 3),
             "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} step(s) of the same workload (route + rotate + gate_up + epilogue, fp64 NumPy), "
+            "sample": f"{done} step(s) of the same workload (route + "
+                      f"{'rotate' if fmt == 'i8h' else 'quantize'} + gate_up + epilogue, fp64 NumPy), "
                       f"{el:.1f} s"}
 
 

@@ -294,6 +294,41 @@ int moe_down_bf16_combine_path(const float* act, int T, int I, const uint16_t* w
 int linear_i8f16(const uint16_t* x, int T, int K, const int8_t* codes, const uint16_t* scales,
                  int N, float* y, void* stream);
 
+/* ------------------------------------------------------------------------
+ * The W8A8 int8 g128 form ("Gemma 4 12B-it · int8 · for radiance", header
+ * table row "Format", and "How it was made", step 2): int8 weights with one
+ * bf16 scale per row and 128 of K, rounded to nearest, no rotation; int8
+ * activations with one scale per token and 128 values. The int5 card's row
+ * "Format" uses such activations above 64 rows: this is the prefill-shaped
+ * form. Readings: the activation scale is float32,
+ *   sx[t, g]   = float32(amax_g / 127)          (IEEE single division)
+ *   qx[t, kk]  = round-half-even(float32(x / sx)), clamped to [-127, 127]
+ * and a group with sx == 0 gets qx = 0. x [T, K] bf16 (16-B aligned), qx
+ * [T, K] int8 out (8-B aligned), sx [T, K/128] float32 out (4-B aligned);
+ * T*K < 2^31 (else I8H_EUNSUPPORTED).
+ * ---------------------------------------------------------------------- */
+int i8_quantize_activations(const uint16_t* x, int T, int K,
+                            int8_t* qx, float* sx, void* stream);
+
+/* Grouped gate_up in the W8A8 form: the call quantizes x (unrotated bf16
+ * [T, K]) as i8_quantize_activations does into the workspace, then
+ *   gu[r, n] = sum_g sw[e, n, g] * sx[t, g] * sum_{kk in g} qw[e, n, kk] * qx[t, kk]
+ * with the epilogue, row order and outputs of moe_gateup_i8h_grouped. The
+ * group sums are exact int32 (int8 MFMA); each is folded into the float32
+ * result with sw * sx. codes [E, N, K] int8 in -127..127, 16-B aligned;
+ * scales [E, N, K/128] bf16, 4-B aligned; N a positive multiple of 64 and
+ * N*K < 2^31 (else I8H_EUNSUPPORTED). Workspace: at least
+ * moe_gateup_i8g_workspace_size(T, K) bytes, 256-B aligned: qx [T, K] int8
+ * at offset 0, sx [T, K/128] float32 at offset round_up(T*K, 256), left there
+ * for the caller. Passes of 192 pairs: one per expert at prefill sizes. */
+size_t moe_gateup_i8g_workspace_size(int T, int K);
+int moe_gateup_i8g_grouped(const uint16_t* x, int T, int K,
+                           const int8_t* codes, const uint16_t* scales,
+                           int E, int N, int topk,
+                           const int32_t* expert_off, const int32_t* sorted_pairs,
+                           float* gate_up, float* act,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

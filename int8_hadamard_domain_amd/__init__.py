@@ -18,6 +18,8 @@ Functions (same names as the C entry points):
                              (the step after the path)
   linear_i8f16               dense int8 linear with f16 group scales (the
                              drafter's linears)
+  i8_quantize_activations    per-token, per-128 int8 activation quantizer (W8A8)
+  moe_gateup_i8g_grouped     grouped W8A8 int8 g128 gate_up + epilogue
 """
 
 import ctypes
@@ -66,6 +68,9 @@ def lib():
         "moe_gateup_fp8blk_workspace_size": (SZ, [I, I]),
         "moe_gateup_fp8blk_grouped": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P, SZ, P]),
         "moe_gateup_fp8blk_grouped_path": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P, SZ, I, P]),
+        "i8_quantize_activations": (I, [P, I, I, P, P, P]),
+        "moe_gateup_i8g_workspace_size": (SZ, [I, I]),
+        "moe_gateup_i8g_grouped": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P, SZ, P]),
         "moe_down_bf16_workspace_size": (SZ, [I, I, I, I]),
         "moe_down_bf16_combine": (I, [P, I, I, P, I, I, I, P, P, P, P, P, P, SZ, P]),
         "moe_down_bf16_combine_path": (I, [P, I, I, P, I, I, I, P, P, P, P, P, P, SZ, I, P]),
@@ -349,3 +354,52 @@ def linear_i8f16(x, codes, scales, out=None):
             raise ValueError(f"out must have shape {(T, N)}")
     _check("linear_i8f16", lib().linear_i8f16(_ptr(x), T, K, _ptr(codes), _ptr(scales), N, _ptr(out), _stream(dev)))
     return out
+
+
+def i8_quantize_activations(x):
+    """x [T, K] bf16 -> (qx int8 [T, K], sx float32 [T, K/128])."""
+    _dev(x, "x", torch.bfloat16, 2)
+    T, K = x.shape
+    qx = torch.empty((T, K), dtype=torch.int8, device=x.device)
+    sx = torch.empty((T, K // 128), dtype=torch.float32, device=x.device)
+    _check("i8_quantize_activations", lib().i8_quantize_activations(
+        _ptr(x), T, K, _ptr(qx), _ptr(sx), _stream(x.device)))
+    return qx, sx
+
+
+def moe_gateup_i8g_grouped(x, codes, scales, topk, expert_off, sorted_pairs,
+                           gate_up=True, act=True, workspace=None):
+    """Grouped W8A8 int8 g128 gate_up.
+
+    x [T, K] bf16 (not rotated), codes [E, N, K] int8, scales [E, N, K/128]
+    bf16. Returns (gate_up, act, workspace); the workspace holds the int8
+    activations and their scales (see i8g_workspace_views).
+    """
+    _dev(x, "x", torch.bfloat16, 2)
+    _dev(codes, "codes", torch.int8, 3)
+    _dev(scales, "scales", torch.bfloat16, 3)
+    _dev(expert_off, "expert_off", torch.int32, 1)
+    _dev(sorted_pairs, "sorted_pairs", torch.int32, 1)
+    T, K = x.shape
+    E, N, K2 = codes.shape
+    if K2 != K or scales.shape != (E, N, K // 128) or expert_off.numel() != E + 1 \
+            or sorted_pairs.numel() != T * topk:
+        raise ValueError("inconsistent shapes")
+    dev = x.device
+    need = lib().moe_gateup_i8g_workspace_size(T, K)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    gu = _out(gate_up, (T * topk, N), dev)
+    ac = _out(act, (T * topk, N // 2), dev)
+    _check("moe_gateup_i8g_grouped", lib().moe_gateup_i8g_grouped(
+        _ptr(x), T, K, _ptr(codes), _ptr(scales), E, N, topk, _ptr(expert_off), _ptr(sorted_pairs),
+        _ptr(gu), _ptr(ac), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return gu, ac, workspace
+
+
+def i8g_workspace_views(workspace, T, K):
+    """(qx [T, K] int8, sx [T, K/128] float32) views of a moe_gateup_i8g_grouped workspace."""
+    a = (T * K + 255) // 256 * 256
+    qx = workspace[:T * K].view(torch.int8).view(T, K)
+    sx = workspace[a:a + T * (K // 128) * 4].view(torch.float32).view(T, K // 128)
+    return qx, sx

@@ -22,7 +22,7 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
          "-I", os.path.join(ROOT, "include")]
 
 SOURCES = ["abi.hip", "route.hip", "fwht.hip", "gateup_i8h_gemv.hip", "gateup_gemm.hip", "gateup_fp8.hip",
-           "down.hip", "linear.hip", "gateup_skinny.hip"]
+           "down.hip", "linear.hip", "gateup_skinny.hip", "gateup_i8g.hip"]
 
 
 def _compile(src):

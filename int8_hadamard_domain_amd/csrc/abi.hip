@@ -87,6 +87,12 @@ struct Fp8Ws {
   }
 };
 
+// W8A8 workspace: qx [T, K] int8, sx [T, K/128] float32
+size_t i8g_sx_off(int T, int K) { return round_up((size_t)T * K, 256); }
+size_t i8g_ws_total(int T, int K) {
+  return i8g_sx_off(T, K) + round_up((size_t)T * (K / 128) * sizeof(float), 256);
+}
+
 }  // namespace
 
 // bf16 grouped down projection + weighted combine
@@ -320,6 +326,43 @@ int moe_gateup_fp8blk_grouped(const uint16_t* x, int T, int K, const uint8_t* co
                               void* stream) {
   return moe_gateup_fp8blk_grouped_path(x, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up, act,
                                         workspace, workspace_bytes, I8H_PATH_AUTO, stream);
+}
+
+// W8A8 int8 g128
+int i8_quantize_activations(const uint16_t* x, int T, int K, int8_t* qx, float* sx, void* stream) {
+  if (T < 0 || K <= 0 || (K % 128) != 0) return I8H_EINVAL;
+  if ((int64_t)T * K >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;
+  if (T == 0) return I8H_OK;
+  if (!x || !qx || !sx || !aligned(x, 16) || !aligned(qx, 8) || !aligned(sx, 4)) return I8H_EINVAL;
+  return from_hip(i8h::launch_i8_act_quant(x, T, K, qx, sx, as_stream(stream)));
+}
+
+size_t moe_gateup_i8g_workspace_size(int T, int K) {
+  if (T <= 0 || K <= 0 || (K % 128) != 0) return 0;
+  return i8g_ws_total(T, K);
+}
+
+int moe_gateup_i8g_grouped(const uint16_t* x, int T, int K, const int8_t* codes, const uint16_t* scales, int E,
+                           int N, int topk, const int32_t* expert_off, const int32_t* sorted_pairs, float* gate_up,
+                           float* act, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_common_moe(T, K, E, N, topk);
+  if (rc != I8H_OK) return rc;
+  if ((N % 64) != 0) return I8H_EINVAL;
+  if ((int64_t)N * K >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;   // one expert's codes, 32-bit offsets
+  if (T == 0) return I8H_OK;
+  if (!x || !codes || !scales || !expert_off || !sorted_pairs) return I8H_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(expert_off, 4) ||
+      !aligned(sorted_pairs, 4))
+    return I8H_EINVAL;
+  if ((gate_up && !aligned(gate_up, 4)) || (act && !aligned(act, 4))) return I8H_EINVAL;
+  if (!workspace || workspace_bytes < i8g_ws_total(T, K) || !aligned(workspace, 256)) return I8H_EINVAL;
+  if (!gate_up && !act) return I8H_OK;
+  int8_t* qx = static_cast<int8_t*>(workspace);
+  float* sx = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + i8g_sx_off(T, K));
+  hipStream_t st = as_stream(stream);
+  if (i8h::launch_i8_act_quant(x, T, K, qx, sx, st) != hipSuccess) return I8H_EHIP;
+  return from_hip(i8h::launch_gateup_i8g(qx, sx, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up,
+                                         act, st));
 }
 
 // bf16 grouped down projection + weighted combine

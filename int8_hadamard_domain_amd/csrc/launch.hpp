@@ -37,6 +37,12 @@ hipError_t launch_gateup_fp8_skinny(const uint16_t* xq, const float* sx, int T, 
                                     const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
                                     const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st);
 
+hipError_t launch_i8_act_quant(const uint16_t* x, int T, int K, int8_t* qx, float* sx, hipStream_t st);
+
+hipError_t launch_gateup_i8g(const int8_t* qx, const float* sx, int T, int K, const int8_t* codes,
+                             const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
+                             const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st);
+
 hipError_t launch_gateup_i8h_gemv_rot(const uint16_t* x, int T, int K, const int8_t* codes,
                                       const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
                                       const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st);

@@ -21,7 +21,7 @@ many-rows (prefill-shaped) form. Readings:
   * the product on the grouped layout of the int8 path:
         gu[r, n] = sum_g sw[e, n, g] * sx[t, g] * sum_{kk in g} qw[e, n, kk] * qx[t, kk]
     with the same GELU-tanh(gate) * up epilogue (gateup.epilogue). The
-    integer group sums are exact (int64 here); the rest rounds at fp64.
+    integer group sums are exact; the rest rounds at fp64.
 """
 
 import numpy as np
@@ -67,7 +67,10 @@ def gateup_i8g(qx, sx, codes, scales, expert_off, sorted_pairs, topk, rows=None)
     codes int8 [E, N, K], scales fp64 [E, N, K/128] (bf16 values).
     Returns gu [R, N] for the requested sorted rows (all P rows by default).
     """
-    qx = np.asarray(qx, dtype=np.int64)
+    # integer-valued fp64 operands: every partial sum of int8 x int8 products
+    # over a group is an integer below 2^21, so the fp64 matmul is exact in
+    # any summation order
+    qx = np.asarray(qx, dtype=np.float64)
     sx = np.asarray(sx, dtype=np.float64)
     n_rows, k_dim = codes.shape[1], codes.shape[2]
     n_groups = k_dim // GROUP
@@ -77,11 +80,11 @@ def gateup_i8g(qx, sx, codes, scales, expert_off, sorted_pairs, topk, rows=None)
     for ex in np.unique(e):
         sel = np.nonzero(e == ex)[0]
         xs = qx[t[sel]].reshape(sel.size, n_groups, GROUP)
-        w = np.asarray(codes[ex], dtype=np.int64).reshape(n_rows, n_groups, GROUP)
+        w = np.asarray(codes[ex], dtype=np.float64).reshape(n_rows, n_groups, GROUP)
         sw = np.asarray(scales[ex], dtype=np.float64)                     # [N, G]
         acc = np.zeros((sel.size, n_rows))
         for g in range(n_groups):
             isum = xs[:, g, :] @ w[:, g, :].T                             # exact integers
-            acc += isum.astype(np.float64) * sw[:, g][None, :] * sx[t[sel], g][:, None]
+            acc += isum * sw[:, g][None, :] * sx[t[sel], g][:, None]
         gu[sel] = acc
     return gu

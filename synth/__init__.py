@@ -15,6 +15,10 @@ gate_up rows per expert; the tiny layer is a small correctness case):
                                            per-expert logit bias N(0, 0.5^2)
   prefill  2048  2048  128  8  1536  3     a prefill chunk
   fp8      128   2048  128  8  1536  4     FP8 block variant, no outliers
+  w8a8     2048  2048  128  8  1536  3     W8A8 int8 g128 form at prefill sizes
+                                           (the prefill chunk's tokens; codes and
+                                           scales drawn as synthetic_i8h, the
+                                           same storage)
 
 Distributions: router logits N(0, 1) float32; activations N(0, 1) rounded to
 bf16, with round(0.01 K) outlier channels (drawn once per layer, shared by
@@ -39,6 +43,7 @@ CONFIGS = {
     "verify":  dict(T=128,  K=2048, E=128, topk=8, N=1536, seed=2, outliers=True,  bias_std=0.5),
     "prefill": dict(T=2048, K=2048, E=128, topk=8, N=1536, seed=3, outliers=True,  bias_std=0.0),
     "fp8":     dict(T=128,  K=2048, E=128, topk=8, N=1536, seed=4, outliers=False, bias_std=0.0),
+    "w8a8":    dict(T=2048, K=2048, E=128, topk=8, N=1536, seed=3, outliers=True,  bias_std=0.0),
 }
 
 

@@ -33,7 +33,7 @@ def L():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -58,6 +58,11 @@ def test_workspace_sizes(L):
     assert L.moe_down_bf16_workspace_size(2048, 768, 2048, 8) == 16384 * 768 * 2 + 16384 * 2048 * 4
     assert L.moe_down_bf16_workspace_size(1, 8, 8, 1) == 256 + 256
     assert L.moe_down_bf16_workspace_size(0, 768, 2048, 8) == 0
+    # W8A8: int8 activations, then their float32 scales, each rounded to 256 B
+    assert L.moe_gateup_i8g_workspace_size(2048, 2048) == 2048 * 2048 + 2048 * 16 * 4
+    assert L.moe_gateup_i8g_workspace_size(3, 128) == 512 + 256
+    assert L.moe_gateup_i8g_workspace_size(0, 2048) == 0
+    assert L.moe_gateup_i8g_workspace_size(4, 100) == 0
 
 
 def route(L, T=8, E=16, k=2, ptr=A, ws=A, wsb=1 << 20):
@@ -198,3 +203,23 @@ def test_linear_validation(L):
     assert f(ODD, 4, 256, A, A, 64, A, None) == EINVAL
     assert f(A, 4, 256, A, ctypes.c_void_p(0x10001), 64, A, None) == EINVAL   # scales 2-B aligned
     assert f(A, 1 << 20, 4096, A, A, 64, A, None) == EUNSUP   # T*K offsets are 32-bit
+
+
+def test_i8g_validation(L):
+    f = L.moe_gateup_i8g_grouped
+    assert f(A, 4, 256, A, A, 8, 224, 2, A, A, A, A, A, 1 << 20, None) == EINVAL    # N % 64
+    assert f(A, 4, 200, A, A, 8, 256, 2, A, A, A, A, A, 1 << 20, None) == EINVAL    # K % 128
+    assert f(A, 4, 256, A, A, 8, 256, 2, A, A, A, A, None, 1 << 20, None) == EINVAL  # no workspace
+    assert f(A, 4, 256, A, A, 8, 256, 2, A, A, A, A, A, 16, None) == EINVAL         # too small
+    assert f(A, 4, 256, A, A, 8, 256, 2, A, A, A, A, ctypes.c_void_p(0x10010), 1 << 20, None) == EINVAL
+    assert f(ODD, 4, 256, A, A, 8, 256, 2, A, A, A, A, A, 1 << 20, None) == EINVAL
+    assert f(A, 4, 256, A, ODD, 8, 256, 2, A, A, A, A, A, 1 << 20, None) == EINVAL
+    assert f(A, 4, 1 << 16, A, A, 8, 1 << 15, 2, A, A, A, A, A, 1 << 30, None) == EUNSUP   # N*K >= 2^31
+    assert f(A, 0, 256, A, A, 8, 256, 2, A, A, A, A, None, 0, None) == OK
+    assert f(A, 4, 256, A, A, 8, 256, 9, A, A, A, A, A, 1 << 20, None) == EUNSUP    # topk > E
+    q = L.i8_quantize_activations
+    assert q(A, 4, 100, A, A, None) == EINVAL
+    assert q(ODD, 4, 128, A, A, None) == EINVAL
+    assert q(A, 4, 128, ctypes.c_void_p(0x10004), A, None) == EINVAL            # qx needs 8-B alignment
+    assert q(A, 1 << 20, 4096, A, A, None) == EUNSUP
+    assert q(A, 0, 128, A, A, None) == OK
