@@ -371,6 +371,7 @@ k_route_gateup_decode(const float* __restrict__ logits, const uint16_t* __restri
                       float* __restrict__ gu, float* __restrict__ act) {
   static_assert(kGemvWaves == 2, "the rotation is shared by two waves");
   __shared__ int s_ids[kWave];
+  __shared__ uint64_t s_rank[kGemvWaves][2 * kWave];                       // top-k scratch, a wave's own
   __shared__ __attribute__((aligned(16))) uint16_t s_xr[NCH * 16 * kWave];  // rotated row, bf16
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
@@ -391,7 +392,7 @@ k_route_gateup_decode(const float* __restrict__ logits, const uint16_t* __restri
     int id;
     float wt;
     if (t != wave) load_logits<VPL>(logits + (size_t)t * E, E, lane, lv);
-    wave_topk<VPL>(lv, E, k, lane, id, wt);
+    wave_topk_fast<VPL>(lv, E, k, lane, id, wt, s_rank[wave]);
     if (lane < k) {
       s_ids[t * k + lane] = id;
       if (writer) {
@@ -402,14 +403,32 @@ k_route_gateup_decode(const float* __restrict__ logits, const uint16_t* __restri
   }
   __syncthreads();
 
-  // group the pairs by expert (each wave on its own, same result everywhere)
+  // group the pairs by expert (each wave on its own, same result everywhere):
+  // below = the first sorted row of the pair's expert, rank = the pair's place
+  // inside it, slot = the expert's place among the non-empty ones, same = the
+  // lanes (pairs) of the expert
   const bool valid = lane < P;
   const int ep = valid ? s_ids[lane] : 0;
-  const PairGroup pg = wave_group_by_expert(valid, ep, bits_for(E));
-  const int below = __popcll(pg.lt);                     // first sorted row of the pair's expert
-  const int rank = __popcll(pg.eq & lanes_below(lane));  // stable rank inside it
-  const uint64_t first = __ballot(valid && rank == 0);   // one lane per non-empty expert
-  const int slot = __popcll(pg.lt & first);              // the expert's place among the non-empty ones
+  int below, rank, slot;
+  uint64_t same;
+  if (T == 1) {
+    // one token: its k experts are distinct and hold one pair each, so the
+    // sorted row and the slot of pair p are the number of chosen experts below
+    // its own (k LDS broadcast reads instead of a ballot per index bit)
+    int c = 0;
+    for (int q = 0; q < P; ++q) c += s_ids[q] < ep;
+    below = c;
+    rank = 0;
+    slot = c;
+    same = 1ull << lane;
+  } else {
+    const PairGroup pg = wave_group_by_expert(valid, ep, bits_for(E));
+    below = __popcll(pg.lt);
+    rank = __popcll(pg.eq & lanes_below(lane));
+    const uint64_t first = __ballot(valid && rank == 0);   // one lane per non-empty expert
+    slot = __popcll(pg.lt & first);
+    same = pg.eq;
+  }
   // the routing outputs: stored by block (0, 0) after its own code loads
   // are on their way (below), or here if it has no rows to work on
   auto store_routing = [&]() {
@@ -435,8 +454,8 @@ k_route_gateup_decode(const float* __restrict__ logits, const uint16_t* __restri
   const int L = __ffsll((unsigned long long)mine) - 1;
   const int e = __builtin_amdgcn_readlane(ep, L);
   const int r0 = __builtin_amdgcn_readlane(below, L);
-  uint64_t rows = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(pg.eq >> 32), L) << 32) |
-                  (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pg.eq, L);
+  uint64_t rows = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(same >> 32), L) << 32) |
+                  (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)same, L);
 
   int p = __ffsll((unsigned long long)rows) - 1;  // pairs of the expert in increasing order
   rows &= rows - 1;

@@ -41,6 +41,12 @@ __device__ __forceinline__ void load_logits(const float* __restrict__ row, int E
   }
 }
 
+// Order-preserving map of a float32 to an unsigned key (+0 and -0 map alike).
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t b = __float_as_uint(v + 0.0f);    // -0 + 0 = +0
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
 template <int VPL>
 __device__ __forceinline__ void wave_topk(const float (&v)[VPL], int E, int k, int lane, int& id, float& weight) {
   uint32_t open = 0;  // bit i: v[i] is a logit not yet taken
@@ -63,6 +69,77 @@ __device__ __forceinline__ void wave_topk(const float (&v)[VPL], int E, int k, i
     }
     if ((best % kWave) == lane) open &= ~(1u << (best / kWave));
     if (lane == j) { my_id = best; my_logit = m; }
+  }
+  const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_logit), 0));
+  float ex = lane < k ? expf(my_logit - l0) : 0.0f;
+  float sum = wave_sum(ex);
+  id = my_id;
+  weight = lane < k ? ex / sum : 0.0f;
+}
+
+// The same top-k, faster when the k largest stand out (the usual case for
+// router logits). The 4 VPL maxima of 16-lane rows (8 maxima of 8-lane
+// groups when VPL == 1) are values of distinct entries, so the smallest of
+// them, tau, is at most the k-th largest when k does not exceed their number:
+// the entries >= tau hold the whole answer, ties at the boundary included.
+// They are written to `scratch` (a wave's own 128 x 8 bytes of LDS) as unique
+// keys (order key << 8 | 255 - index: larger value first, then lower index),
+// each ranked by counting the keys above it, and the first k are taken in
+// rank order. More than 64 candidates, k above the number of groups, or a
+// NaN or -inf tau fall back to wave_topk. Same ids and weights as wave_topk.
+template <int VPL>
+__device__ __forceinline__ void wave_topk_fast(const float (&v)[VPL], int E, int k, int lane, int& id, float& weight,
+                                               uint64_t* scratch) {
+  constexpr int kGroups = VPL == 1 ? 8 : 4 * VPL;
+  float tau = INFINITY;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    float m = lane + kWave * i < E ? v[i] : -INFINITY;
+    m = fmaxf(m, xor_lane<1>(m));
+    m = fmaxf(m, xor_lane<2>(m));
+    m = fmaxf(m, xor_lane<4>(m));
+    if constexpr (VPL > 1) m = fmaxf(m, xor_lane<8>(m));
+    tau = fminf(tau, m);
+  }
+  if constexpr (VPL == 1) tau = fminf(tau, xor_lane<8>(tau));
+  tau = fminf(tau, xor_lane<16>(tau));
+  tau = fminf(tau, xor_lane<32>(tau));
+  uint64_t cm[VPL];
+  int C = 0;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    cm[i] = __ballot(lane + kWave * i < E && v[i] >= tau);
+    C += __popcll(cm[i]);
+  }
+  if (k > kGroups || C > kWave || !(tau > -INFINITY)) {
+    wave_topk<VPL>(v, E, k, lane, id, weight);
+    return;
+  }
+  // candidates in index order, element i of lane l after every earlier one
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    if ((cm[i] >> lane) & 1) {
+      const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(cm[i] >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)cm[i], 0u));
+      scratch[pos] = ((uint64_t)order_key(v[i]) << 8) | (uint64_t)(255 - (lane + kWave * i));
+    }
+    base += __popcll(cm[i]);
+  }
+  __builtin_amdgcn_wave_barrier();
+  const uint64_t mine = lane < C ? scratch[lane] : 0ull;
+  int r = 0;
+  for (int j = 0; j < C; ++j) r += scratch[j] > mine ? 1 : 0;
+  __builtin_amdgcn_wave_barrier();
+  if (lane < C && r < k) scratch[kWave + r] = mine;
+  __builtin_amdgcn_wave_barrier();
+  int my_id = -1;
+  float my_logit = 0.0f;
+  if (lane < k) {
+    const uint64_t t = scratch[kWave + lane];
+    const uint32_t key = (uint32_t)(t >> 8);
+    my_id = 255 - (int)(t & 0xffu);
+    my_logit = __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
   }
   const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_logit), 0));
   float ex = lane < k ? expf(my_logit - l0) : 0.0f;

@@ -86,6 +86,34 @@ def test_logit_ties(gpu_available):
     _run(L, lg=lg.astype(np.float32), what="ties")
 
 
+@pytest.mark.parametrize("case", ["rounded", "fully_tied", "signed_zeros", "top_block_tied", "minus_inf"])
+def test_one_token_ties(gpu_available, case):
+    # one token: the threshold/candidate top-k and its exact fallback (more
+    # than 64 candidates, or a -inf threshold) against the oracle's order
+    L = synth.layer("decode", K=256, N=64)
+    lg = synth.router_logits(L).copy()
+    if case == "rounded":
+        lg = np.round(lg, 1)
+    elif case == "fully_tied":
+        lg[:] = 0.25
+    elif case == "signed_zeros":
+        lg[0, ::2] = -0.0
+        lg[0, 1::2] = 0.0
+        lg[0, 77] = 1.0
+    elif case == "top_block_tied":
+        lg[0, [3, 90, 17, 64, 120]] = 9.0
+    else:
+        lg[0, :100] = -np.inf
+    _run(L, lg=lg.astype(np.float32), what=f"one token {case}")
+
+
+def test_one_token_many_rows(gpu_available):
+    # the decode workload's logits, many tokens one at a time
+    for seed in range(24):
+        L = synth.layer("decode", K=256, N=64, seed=100 + seed)
+        _run(L, what=f"one token seed {100 + seed}")
+
+
 def test_skewed_experts(gpu_available):
     # all tokens on the same few experts: several rows per expert
     L = synth.layer("verify", T=8, K=1024, E=128, topk=8, N=512, bias_std=0.0)
