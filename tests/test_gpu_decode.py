@@ -71,6 +71,9 @@ def test_tiny_layer(gpu_available):
     (2, 384, 16, 3, 128),      # pieces past K in the last (partial) chunk
     (1, 128, 1, 1, 64),        # one expert, one group
     (5, 256, 8, 8, 192),       # every expert chosen by every token
+    (4, 1024, 256, 16, 512),   # k = 16 from 16 row maxima (the threshold top-k at its limit)
+    (4, 1024, 128, 16, 512),   # k above the 8 row maxima: the round-based top-k
+    (2, 512, 64, 32, 128),     # one logit per lane, k = 32: the round-based top-k
 ])
 def test_shapes(gpu_available, T, K, E, k, N):
     _run(synth.layer("verify", T=T, K=K, E=E, topk=k, N=N, bias_std=0.0), what="shape")
