@@ -26,6 +26,11 @@
  *   - Calls are thread-safe and reentrant; calls on different streams may
  *     overlap as long as their output buffers do not alias.
  *   - Row-major layouts throughout; the last index is contiguous.
+ *   - bf16 scale arrays (4-byte aligned, as each call requires) are read by
+ *     the MFMA kernels in aligned 4-byte words: when a scale array holds an
+ *     odd number of elements, the 2 bytes after its last element are read
+ *     (never used, never written). Allocations of HIP and torch are rounded
+ *     to at least 256 bytes, so such a read stays inside the allocation.
  *
  * Sizes: T tokens, K hidden size (K % 128 == 0), E experts (1..1024),
  * topk experts per token (1..min(E, 32)), N = 2*I gate_up rows per expert
