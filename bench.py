@@ -71,7 +71,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures the hot path on ONE GPU; --gpus must be 1 "
+        print("bench.py: the hot path is measured on one GPU; --gpus must be 1 "
               f"(got --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
 
