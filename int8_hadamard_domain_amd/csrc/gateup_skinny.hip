@@ -27,8 +27,11 @@
 //
 // Stage layouts as in the larger kernels: A piece p (8 bf16) of row r (128
 // bytes) at p ^ ((r >> 1) & 7), B piece p (16 codes) of row r (64 bytes) at
-// p ^ ((r >> 2) & 3); MFMA k-step s reads A piece 2 s + half and B codes
-// 16 s + 8 half .. +7, so both operands agree on every k.
+// p ^ ((r >> 2) & 3). Within a 64-K stage, MFMA k-step s takes
+// k = 32 half + 8 s .. +7 in the lanes of half `half` (lane / 32): a B lane
+// reads one contiguous 32-byte span of its row (pieces 2 half, 2 half + 1;
+// sixteen consecutive rows then cover all 64 banks) and an A lane piece
+// 4 half + s, so both operands agree on every k.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -239,14 +242,24 @@ __device__ __forceinline__ void skinny_body(const uint16_t* __restrict__ xa, con
 #pragma unroll
           for (int j = 0; j < 16; ++j) tmp[c][j] = 0.0f;
       }
+      // the lane's 32 codes of the stage (k = 32 half .. +31): pieces 2 half
+      // and 2 half + 1 of its gate and up rows
+      u32x4 cg[2], cu[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        cg[q] = *reinterpret_cast<const u32x4*>(&bbuf[rg * kSStageK + 16 * sb_pos(rg, 2 * half + q)]);
+        cu[q] = *reinterpret_cast<const u32x4*>(&bbuf[ru * kSStageK + 16 * sb_pos(ru, 2 * half + q)]);
+      }
+      const int m = mw + col;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const u32x2 cgw = *reinterpret_cast<const u32x2*>(&bbuf[rg * kSStageK + 16 * sb_pos(rg, s) + 8 * half]);
-        const u32x2 cuw = *reinterpret_cast<const u32x2*>(&bbuf[ru * kSStageK + 16 * sb_pos(ru, s) + 8 * half]);
-        const int m = mw + col;
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&abuf[m * kSStageK + 8 * sa_pos(m, 2 * s + half)]);
-        tmp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, s_decode<F>(cgw[0], cgw[1]), tmp[0], 0, 0, 0);
-        tmp[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, s_decode<F>(cuw[0], cuw[1]), tmp[1], 0, 0, 0);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&abuf[m * kSStageK + 8 * sa_pos(m, 4 * half + s)]);
+        const u32x4& g4 = cg[s / 2];
+        const u32x4& u4 = cu[s / 2];
+        tmp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, s_decode<F>(g4[2 * (s % 2)], g4[2 * (s % 2) + 1]),
+                                                         tmp[0], 0, 0, 0);
+        tmp[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, s_decode<F>(u4[2 * (s % 2)], u4[2 * (s % 2) + 1]),
+                                                         tmp[1], 0, 0, 0);
       }
       if (h & 1) {
         const int g = h / 2;
