@@ -37,8 +37,11 @@
 // significand bits), E4M3 by v_cvt_pk_f32_fp8 (3 significand bits).
 //
 // MFMA operands (32x32x16 bf16): lane l feeds 8 values of row (A) or column
-// (B) l % 32 for k = 16 s + 8 (l / 32) + j in step s; the 32x32 result sits
-// in lane l as column l % 32, rows 8 (j / 4) + 4 (l / 32) + j % 4.
+// (B) l % 32 for step s; within a 64-K stage the lanes of half h = l / 32
+// take k = 32 h + 8 s + j, so a B lane reads its stage's codes as one
+// contiguous 32-byte span (16 consecutive rows then cover all 64 LDS banks)
+// and an A lane piece 4 h + s. The 32x32 result sits in lane l as column
+// l % 32, rows 8 (j / 4) + 4 (l / 32) + j % 4.
 
 #include <type_traits>
 
@@ -277,16 +280,20 @@ k_gateup_gemm(const uint16_t* __restrict__ xa, const float* __restrict__ sx, int
 #pragma unroll
             for (int j = 0; j < 16; ++j) tmp[a][c][j] = 0.0f;
       }
+      // the lane's 32 codes of the stage (k = 32 half .. +31) are pieces
+      // 2 half and 2 half + 1 of its gate and up rows: piece q serves k-steps
+      // 2 q and 2 q + 1
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const u32x2 cgw = *reinterpret_cast<const u32x2*>(&bbuf[rg * kStageK + 16 * b_pos(rg, s) + 8 * half]);
-        const u32x2 cuw = *reinterpret_cast<const u32x2*>(&bbuf[ru * kStageK + 16 * b_pos(ru, s) + 8 * half]);
-        const bf16x8 wg = decode8<F>(cgw[0], cgw[1]);
-        const bf16x8 wu = decode8<F>(cuw[0], cuw[1]);
+        u32x4 cg, cu;
+        cg = *reinterpret_cast<const u32x4*>(&bbuf[rg * kStageK + 16 * b_pos(rg, 2 * half + s / 2)]);
+        cu = *reinterpret_cast<const u32x4*>(&bbuf[ru * kStageK + 16 * b_pos(ru, 2 * half + s / 2)]);
+        const bf16x8 wg = decode8<F>(cg[2 * (s % 2)], cg[2 * (s % 2) + 1]);
+        const bf16x8 wu = decode8<F>(cu[2 * (s % 2)], cu[2 * (s % 2) + 1]);
 #pragma unroll
         for (int a = 0; a < kMTiles; ++a) {
           const int m = mw + 32 * a + col;
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(&abuf[m * kStageK + 8 * a_pos(m, 2 * s + half)]);
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(&abuf[m * kStageK + 8 * a_pos(m, 4 * half + s)]);
           tmp[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, wg, tmp[a][0], 0, 0, 0);
           tmp[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, wu, tmp[a][1], 0, 0, 0);
         }
