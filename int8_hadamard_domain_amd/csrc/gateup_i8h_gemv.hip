@@ -34,7 +34,7 @@
 // token), groups the pairs by expert with ballots, picks the expert of its
 // slot and goes on as above; block (0, 0) also stores the routing outputs.
 // One launch then covers route -> rotate -> gate_up, and no block waits for
-// another kernel's results. The two waves of a block split the rotation of a
+// another kernel's results. The four waves of a block split the rotation of a
 // token row and share it through LDS; with a single token the row is fetched
 // before the routing, and the rotation runs after the code loads are issued.
 
@@ -47,6 +47,13 @@ namespace i8h {
 
 constexpr int kGemvThreads = 128;  // two waves: the decode grid spreads evenly over the CUs
 constexpr int kGemvWaves = kGemvThreads / kWave;
+// The routed decode kernel: every workgroup repeats the routing and the
+// rotation of the token row, so four waves share them (half of that work
+// per streamed byte against two-wave workgroups). A workgroup covers
+// kDecWaves * RPW row pairs, which divides I (N % 64 == 0), so all of its
+// waves have rows or none has.
+constexpr int kDecThreads = 256;
+constexpr int kDecWaves = kDecThreads / kWave;
 constexpr int kScanChunks = 4;  // expert_off entries per lane and round trip (E <= 256 in one)
 
 // Expert owning the s-th non-empty run of expert_off (in expert order), with
@@ -302,18 +309,19 @@ k_gateup_i8h_gemv(const uint16_t* __restrict__ xin, int K, const int8_t* __restr
   }
 }
 
-// The rotation of one token row is shared by the two waves of a block: wave
-// w rotates the pieces c = w, w + 2, .. (64 lanes x 16 values each) and
-// leaves them as bf16 in LDS, where both waves read the whole row.
+// The rotation of one token row is shared by the waves of a workgroup: wave
+// w rotates the pieces c = w, w + kDecWaves, .. (64 lanes x 16 values each)
+// and leaves them as bf16 in LDS, where every wave reads the whole row.
 template <int NCH>
 struct RotShare {
-  static constexpr int kN = (NCH + 1) / 2;
+  static constexpr int kN = (NCH + kDecWaves - 1) / kDecWaves;
   XRow<kN> X;
 
   __device__ __forceinline__ void load(const uint16_t* __restrict__ xr, int K, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
-      const int kk = min(16 * (lane + kWave * (wave + 2 * i)), K - 16);  // past K: a copy (weight 0 later)
+      if (wave + kDecWaves * i >= NCH) break;  // uniform in the wave
+      const int kk = min(16 * (lane + kWave * (wave + kDecWaves * i)), K - 16);  // past K: a copy (weight 0 later)
       X.a[i] = *reinterpret_cast<const u32x4*>(xr + kk);
       X.b[i] = *reinterpret_cast<const u32x4*>(xr + kk + 8);
     }
@@ -322,7 +330,7 @@ struct RotShare {
   __device__ __forceinline__ void rotate_to(uint16_t* s_xr, int wave, int lane) const {
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
-      const int c = wave + 2 * i;
+      const int c = wave + kDecWaves * i;
       if (c >= NCH) break;  // uniform in the wave
       float xv[16];
 #pragma unroll
@@ -363,15 +371,15 @@ __device__ __forceinline__ void read_rotated(const uint16_t* s_xr, float (&xv)[N
 }
 
 template <int NCH, int RPW, int VPL>
-__global__ void __launch_bounds__(kGemvThreads)
+__global__ void __launch_bounds__(kDecThreads)
 k_route_gateup_decode(const float* __restrict__ logits, const uint16_t* __restrict__ x, int T, int K,
                       const int8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int E, int N, int k,
                       int32_t* __restrict__ ids_out, float* __restrict__ w_out, int32_t* __restrict__ expert_off,
                       int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos,
                       float* __restrict__ gu, float* __restrict__ act) {
-  static_assert(kGemvWaves == 2, "the rotation is shared by two waves");
+  static_assert(32 % (kDecWaves * RPW) == 0, "a workgroup's row pairs divide I");
   __shared__ int s_ids[kWave];
-  __shared__ uint64_t s_rank[kGemvWaves][2 * kWave];                       // top-k scratch, a wave's own
+  __shared__ uint64_t s_rank[kDecWaves][2 * kWave];                       // top-k scratch, a wave's own
   __shared__ __attribute__((aligned(16))) uint16_t s_xr[NCH * 16 * kWave];  // rotated row, bf16
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
@@ -388,7 +396,7 @@ k_route_gateup_decode(const float* __restrict__ logits, const uint16_t* __restri
   if (T == 1) share.load(x, K, wave, lane);
 
   // top-k of every token, a wave per token
-  for (int t = wave; t < T; t += kGemvWaves) {
+  for (int t = wave; t < T; t += kDecWaves) {
     int id;
     float wt;
     if (t != wave) load_logits<VPL>(logits + (size_t)t * E, E, lane, lv);
@@ -437,16 +445,16 @@ k_route_gateup_decode(const float* __restrict__ logits, const uint16_t* __restri
       pair_pos[lane] = below + rank;
     }
     // expert_off[e] = number of pairs routed to experts below e
-    for (int e = threadIdx.x; e <= E; e += kGemvThreads) {
+    for (int e = threadIdx.x; e <= E; e += kDecThreads) {
       int c = 0;
       for (int q = 0; q < P; ++q) c += s_ids[q] < e;
       expert_off[e] = c;
     }
   };
-  // both waves of a block see the same slot and (I % 8 == 0) the same i0 range,
-  // so they leave together and meet at the barriers below
+  // all waves of a workgroup see the same slot and (kDecWaves * RPW divides
+  // I) the same i0 range, so they leave together and meet at the barriers below
   const uint64_t mine = __ballot(valid && rank == 0 && slot == (int)blockIdx.y);
-  const int i0 = (blockIdx.x * kGemvWaves + wave) * RPW;
+  const int i0 = (blockIdx.x * kDecWaves + wave) * RPW;
   if (mine == 0 || i0 >= I) {
     if (writer) store_routing();
     return;
@@ -466,7 +474,7 @@ k_route_gateup_decode(const float* __restrict__ logits, const uint16_t* __restri
   __builtin_amdgcn_sched_barrier(0);
   if (writer) store_routing();
   for (int r = r0; p >= 0; ++r) {
-    if (r != r0) __syncthreads();        // the previous row is read by both waves
+    if (r != r0) __syncthreads();        // the previous row is read by every wave
     share.rotate_to(s_xr, wave, lane);   // runs while the codes arrive
     __syncthreads();
     float xv[NCH][16];
@@ -521,9 +529,9 @@ static void launch_decode(dim3 grid, int vpl, const float* logits, const uint16_
                           int32_t* expert_off, int32_t* sorted_pairs, int32_t* pair_pos, float* gu, float* act,
                           hipStream_t st) {
 #define I8H_DECODE_ARGS logits, x, T, K, codes, scales, E, N, k, ids, w, expert_off, sorted_pairs, pair_pos, gu, act
-  if (vpl <= 1) k_route_gateup_decode<NCH, RPW, 1><<<grid, kGemvThreads, 0, st>>>(I8H_DECODE_ARGS);
-  else if (vpl <= 2) k_route_gateup_decode<NCH, RPW, 2><<<grid, kGemvThreads, 0, st>>>(I8H_DECODE_ARGS);
-  else k_route_gateup_decode<NCH, RPW, 4><<<grid, kGemvThreads, 0, st>>>(I8H_DECODE_ARGS);
+  if (vpl <= 1) k_route_gateup_decode<NCH, RPW, 1><<<grid, kDecThreads, 0, st>>>(I8H_DECODE_ARGS);
+  else if (vpl <= 2) k_route_gateup_decode<NCH, RPW, 2><<<grid, kDecThreads, 0, st>>>(I8H_DECODE_ARGS);
+  else k_route_gateup_decode<NCH, RPW, 4><<<grid, kDecThreads, 0, st>>>(I8H_DECODE_ARGS);
 #undef I8H_DECODE_ARGS
 }
 
@@ -537,13 +545,13 @@ hipError_t launch_route_gateup_decode(const float* logits, const uint16_t* x, in
   int nch = cdiv(K, 16 * kWave);
   int vpl = cdiv(E, kWave);
   if (nch <= 1) {
-    launch_decode<1, 4>(dim3(cdiv(I, kGemvWaves * 4), slots), vpl, logits, x, T, K, codes, scales, E, N, k, ids, w,
+    launch_decode<1, 4>(dim3(cdiv(I, kDecWaves * 4), slots), vpl, logits, x, T, K, codes, scales, E, N, k, ids, w,
                         expert_off, sorted_pairs, pair_pos, gu, act, st);
   } else if (nch <= 2) {
-    launch_decode<2, 2>(dim3(cdiv(I, kGemvWaves * 2), slots), vpl, logits, x, T, K, codes, scales, E, N, k, ids, w,
+    launch_decode<2, 2>(dim3(cdiv(I, kDecWaves * 2), slots), vpl, logits, x, T, K, codes, scales, E, N, k, ids, w,
                         expert_off, sorted_pairs, pair_pos, gu, act, st);
   } else {
-    launch_decode<4, 2>(dim3(cdiv(I, kGemvWaves * 2), slots), vpl, logits, x, T, K, codes, scales, E, N, k, ids, w,
+    launch_decode<4, 2>(dim3(cdiv(I, kDecWaves * 2), slots), vpl, logits, x, T, K, codes, scales, E, N, k, ids, w,
                         expert_off, sorted_pairs, pair_pos, gu, act, st);
   }
   return hipGetLastError();
