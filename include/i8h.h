@@ -27,7 +27,7 @@
  *     overlap as long as their output buffers do not alias.
  *   - Row-major layouts throughout; the last index is contiguous.
  *   - bf16 scale arrays (4-byte aligned, as each call requires) are read by
- *     the MFMA kernels in aligned 4-byte words: when a scale array holds an
+ *     the MFMA and GEMV kernels in aligned 4-byte words: when a scale array holds an
  *     odd number of elements, the 2 bytes after its last element are read
  *     (never used, never written). Allocations of HIP and torch are rounded
  *     to at least 256 bytes, so such a read stays inside the allocation.

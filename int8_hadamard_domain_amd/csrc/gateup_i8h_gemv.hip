@@ -125,14 +125,20 @@ __device__ __forceinline__ void rotate16(float (&xv)[16], int lane) {
   }
 }
 
-// Codes and scales of one wave's RPW row pairs, held in registers (scales as
-// their bf16 bits: converting them where they are loaded would make the wave
-// wait for the whole code stream before it can issue anything else).
+// Codes and scales of one wave's RPW row pairs, held in registers. A scale
+// is kept as the aligned 4-byte word holding its bf16 bits and converted
+// where it is used: converting it where it is loaded would make the wave wait
+// for the load before it can do anything else.
 template <int NCH, int RPW>
 struct WaveRows {
   u32x4 cg[RPW][NCH], cu[RPW][NCH];
   uint32_t sg[RPW][NCH], su[RPW][NCH];
 };
+
+// The bf16 scale held in the high half of word w when odd, else in the low half.
+__device__ __forceinline__ float scale_of_word(uint32_t w, int odd) {
+  return __uint_as_float(odd ? (w & 0xffff0000u) : (w << 16));
+}
 
 // One token row as the lane reads it: the 16 values kk = 16 (lane + 64 c) ..
 template <int NCH>
@@ -145,15 +151,16 @@ __device__ __forceinline__ void load_rows(WaveRows<NCH, RPW>& R, const int8_t* _
                                           const uint16_t* __restrict__ scales, int e, int N, int K, int i0,
                                           int lane) {
   const int I = N / 2, G = K / kGroup;
+  const uint32_t* sw = reinterpret_cast<const uint32_t*>(scales);  // 4-byte aligned
 #pragma unroll
   for (int j = 0; j < RPW; ++j) {
-    const uint16_t* srg = scales + ((size_t)e * N + i0 + j) * G;
-    const uint16_t* sru = scales + ((size_t)e * N + I + i0 + j) * G;
+    const size_t rg = ((size_t)e * N + i0 + j) * G;
+    const size_t ru = ((size_t)e * N + I + i0 + j) * G;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int g = min(16 * (lane + kWave * c), K - 16) / kGroup;
-      R.sg[j][c] = srg[g];
-      R.su[j][c] = sru[g];
+      R.sg[j][c] = sw[(rg + g) >> 1];
+      R.su[j][c] = sw[(ru + g) >> 1];
     }
   }
   // in the order the dot products consume them (piece-major): loads complete
@@ -204,7 +211,7 @@ template <int NCH, int RPW>
 __device__ __forceinline__ void gemv_row(const WaveRows<NCH, RPW>& R, const float (&xv)[NCH][16], int K, int N,
                                          int i0, size_t r, float* __restrict__ gu, float* __restrict__ act,
                                          int lane) {
-  const int I = N / 2;
+  const int I = N / 2, G = K / kGroup;
   float v[2 * RPW];
 #pragma unroll
   for (int q = 0; q < 2 * RPW; ++q) v[q] = 0.0f;
@@ -212,12 +219,16 @@ __device__ __forceinline__ void gemv_row(const WaveRows<NCH, RPW>& R, const floa
   for (int c = 0; c < NCH; ++c) {
     // a piece past K (a copy of the last one: finite) counts with weight 0
     const bool inside = 16 * (lane + kWave * c) < K;
+    const int g = min(16 * (lane + kWave * c), K - 16) / kGroup;
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
-      // the codes are loop-invariant over rows; an empty asm keeps their
-      // conversion here (hoisted, it would hold every code as a float)
+      // the codes and scales are loop-invariant over rows; an empty asm keeps
+      // their conversion here (hoisted, it would hold every code as a float,
+      // and the scales' conversion would make the wave wait for their loads
+      // before the activation row is prepared)
       u32x4 qg = R.cg[j][c], qu = R.cu[j][c];
-      asm volatile("" : "+v"(qg), "+v"(qu));
+      uint32_t sg = R.sg[j][c], su = R.su[j][c];
+      asm volatile("" : "+v"(qg), "+v"(qu), "+v"(sg), "+v"(su));
       float pg0 = 0.0f, pg1 = 0.0f, pu0 = 0.0f, pu1 = 0.0f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -230,8 +241,12 @@ __device__ __forceinline__ void gemv_row(const WaveRows<NCH, RPW>& R, const floa
         pu0 = fmaf(sbyte<2>(qu[w]), xv[c][4 * w + 2], pu0);
         pu1 = fmaf(sbyte<3>(qu[w]), xv[c][4 * w + 3], pu1);
       }
-      v[2 * j] = fmaf(inside ? bf16_lo(R.sg[j][c]) : 0.0f, pg0 + pg1, v[2 * j]);
-      v[2 * j + 1] = fmaf(inside ? bf16_lo(R.su[j][c]) : 0.0f, pu0 + pu1, v[2 * j + 1]);
+      // the element index (e N + i0 + j) G + g of the gate scale and the one
+      // of the up scale (I rows later) have the parity of (i0 + j) G + g: N
+      // and I are even
+      const int odd = (((i0 + j) & G) ^ g) & 1;
+      v[2 * j] = fmaf(inside ? scale_of_word(sg, odd) : 0.0f, pg0 + pg1, v[2 * j]);
+      v[2 * j + 1] = fmaf(inside ? scale_of_word(su, odd) : 0.0f, pu0 + pu1, v[2 * j + 1]);
     }
   }
   // v = (g0, u0, g1, u1, ...): fold halves over bits 5, 4 (and 3), then sum
