@@ -146,32 +146,43 @@ struct XRow {
   u32x4 a[NCH], b[NCH];
 };
 
+// A wave-uniform 64-bit value, held in scalar registers.
+__device__ __forceinline__ size_t uniform_size(size_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((size_t)hi << 32) | lo;
+}
+
 template <int NCH, int RPW>
 __device__ __forceinline__ void load_rows(WaveRows<NCH, RPW>& R, const int8_t* __restrict__ codes,
                                           const uint16_t* __restrict__ scales, int e, int N, int K, int i0,
                                           int lane) {
+  // row bases are wave-uniform (scalar registers); a lane adds a 32-bit
+  // offset, so every load takes the scalar-base form
   const int I = N / 2, G = K / kGroup;
   const uint32_t* sw = reinterpret_cast<const uint32_t*>(scales);  // 4-byte aligned
 #pragma unroll
   for (int j = 0; j < RPW; ++j) {
-    const size_t rg = ((size_t)e * N + i0 + j) * G;
-    const size_t ru = ((size_t)e * N + I + i0 + j) * G;
+    const size_t rg = ((size_t)e * N + i0 + j) * G;  // element index of the row's first scale
+    const size_t ru = rg + (size_t)I * G;
+    const uint32_t* swg = sw + (rg >> 1);
+    const uint32_t* swu = sw + (ru >> 1);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int g = min(16 * (lane + kWave * c), K - 16) / kGroup;
-      R.sg[j][c] = sw[(rg + g) >> 1];
-      R.su[j][c] = sw[(ru + g) >> 1];
+      const uint32_t g = (uint32_t)min(16 * (lane + kWave * c), K - 16) / kGroup;
+      R.sg[j][c] = swg[(((uint32_t)rg & 1u) + g) >> 1];
+      R.su[j][c] = swu[(((uint32_t)ru & 1u) + g) >> 1];
     }
   }
   // in the order the dot products consume them (piece-major): loads complete
   // in issue order, so the first pieces can be used while the rest arrive
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const int kk = min(16 * (lane + kWave * c), K - 16);  // pieces past K re-read the last one
+    const uint32_t kk = (uint32_t)min(16 * (lane + kWave * c), K - 16);  // pieces past K re-read the last one
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
-      const int8_t* rowg = codes + ((size_t)e * N + i0 + j) * K;
-      const int8_t* rowu = codes + ((size_t)e * N + I + i0 + j) * K;
+      const int8_t* rowg = codes + uniform_size(((size_t)e * N + i0 + j) * K);
+      const int8_t* rowu = codes + uniform_size(((size_t)e * N + I + i0 + j) * K);
       R.cg[j][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowg + kk));
       R.cu[j][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowu + kk));
     }
@@ -296,7 +307,7 @@ k_gateup_i8h_gemv(const uint16_t* __restrict__ xin, int K, const int8_t* __restr
                   float* __restrict__ gu, float* __restrict__ act) {
   static_assert(RPW == 2 || RPW == 4, "2*RPW values per lane are folded over bits 5..");
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: row bases in SGPRs
   const int I = N / 2;
   const int i0 = (blockIdx.x * kGemvWaves + wave) * RPW;  // I % RPW == 0, so all RPW rows exist
   if (i0 >= I) return;
@@ -397,7 +408,7 @@ k_route_gateup_decode(const float* __restrict__ logits, const uint16_t* __restri
   __shared__ uint64_t s_rank[kDecWaves][2 * kWave];                       // top-k scratch, a wave's own
   __shared__ __attribute__((aligned(16))) uint16_t s_xr[NCH * 16 * kWave];  // rotated row, bf16
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: row bases in SGPRs
   const int I = N / 2;
   const bool writer = blockIdx.x == 0 && blockIdx.y == 0;  // stores the routing outputs
   const int P = T * k;                                     // <= 64
