@@ -5,7 +5,8 @@
 // projections in bf16. W_down[e] is [H, I] row-major (H = the hidden size);
 // the float32 act rows of the gate_up epilogue are rounded to bf16 (nearest
 // even) for the product, which accumulates in float32 (products of two bf16
-// values are exact in float32):
+// values are exact in float32; the few-pairs form adds them two at a time
+// with v_dot2_f32_bf16):
 //   y[r, h]   = sum_i W_down[e(r), h, i] * bf16(act[r, i])      (sorted row r)
 //   out[t, h] = sum_j w[t, j] * y[pos[t k + j], h]              (slot order j)
 //
@@ -40,6 +41,14 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // Few pairs: out[t, h0 .. h0 + 7] of one token per workgroup.
 
 constexpr int kDvRows = 8;       // output rows per workgroup
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// c + a.lo * b.lo + a.hi * b.hi for two pairs of bf16 values (v_dot2_f32_bf16:
+// one instruction per two products, on the packed pairs as loaded)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
 constexpr int kDvThreads = 256;  // 8 half-waves
 
 // NQ: 16-byte pieces (8 bf16) per lane per row, I <= 256 * NQ
@@ -62,11 +71,12 @@ k_down_gemv_combine(const float* __restrict__ act, int I, const uint16_t* __rest
     for (int row = 0; row < kDvRows; ++row)
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        const int c = l + 32 * q;
-        wv[row][q] = c < npc ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr + (size_t)row * I + 8 * c))
-                             : u32x4{0u, 0u, 0u, 0u};
+        // a piece past the row re-reads the last one (finite; its act pair is zero)
+        const int c = min(l + 32 * q, npc - 1);
+        wv[row][q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr + (size_t)row * I + 8 * c));
       }
-    float a[NQ][8];
+    // the act values rounded to bf16 (nearest even), in pairs as the weights are
+    uint32_t a[NQ][4];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int c = l + 32 * q;
@@ -75,15 +85,10 @@ k_down_gemv_combine(const float* __restrict__ act, int I, const uint16_t* __rest
         lo = *reinterpret_cast<const f32x4*>(act + (size_t)r * I + 8 * c);
         hi = *reinterpret_cast<const f32x4*>(act + (size_t)r * I + 8 * c + 4);
       }
-      // round to bf16 (nearest even), keep the rounded values as floats
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint32_t p0 = pack_bf16x2(lo[2 * i], lo[2 * i + 1]), p1 = pack_bf16x2(hi[2 * i], hi[2 * i + 1]);
-        a[q][2 * i] = bf16_lo(p0);
-        a[q][2 * i + 1] = bf16_hi(p0);
-        a[q][4 + 2 * i] = bf16_lo(p1);
-        a[q][4 + 2 * i + 1] = bf16_hi(p1);
-      }
+      a[q][0] = pack_bf16x2(lo[0], lo[1]);
+      a[q][1] = pack_bf16x2(lo[2], lo[3]);
+      a[q][2] = pack_bf16x2(hi[0], hi[1]);
+      a[q][3] = pack_bf16x2(hi[2], hi[3]);
     }
 #pragma unroll
     for (int row = 0; row < kDvRows; ++row) {
@@ -91,10 +96,7 @@ k_down_gemv_combine(const float* __restrict__ act, int I, const uint16_t* __rest
 #pragma unroll
       for (int q = 0; q < NQ; ++q)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          s = fmaf(bf16_lo(wv[row][q][i]), a[q][2 * i], s);
-          s = fmaf(bf16_hi(wv[row][q][i]), a[q][2 * i + 1], s);
-        }
+        for (int i = 0; i < 4; ++i) s = dot2_bf16(wv[row][q][i], a[q][i], s);
       s += xor_lane<1>(s);
       s += xor_lane<2>(s);
       s += xor_lane<4>(s);
