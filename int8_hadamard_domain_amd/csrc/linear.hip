@@ -4,14 +4,17 @@
 //   y[t, n] = sum_g s[n, g] * sum_{k in g} q[n, k] * x[t, k]      (x bf16, y float32)
 //
 // The drafter runs a block of 16 positions at a time, so the product is a
-// skinny GEMM: one workgroup owns 16 output columns x 16 tokens, and its four
-// waves split the K groups (wave w takes g = w, w + 4, ...). Per group a wave
+// skinny GEMM: one workgroup owns 16 output columns x 16 tokens, and its eight
+// waves split the K groups (wave w takes g = w, w + 8, ...): more waves per
+// CU keep more loads in flight than four (6.1 against 6.5 us at the drafter
+// shape; wider workgroups, which read each activation tile fewer times, left
+// CUs idle and were slower). Per group a wave
 // runs four v_mfma_f32_16x16x32_bf16 on codes decoded to bf16 (exact), from a
 // zero accumulator, then folds that group's partial into its float32 result
 // with the column's f16 scale (4 FMAs a lane). Within a group, lane quarter q
 // takes the 32 contiguous K positions 32 q .. 32 q + 31 (MFMA i reads 8 q' +
 // 0..7 of its window from the lane's 8 i .. 8 i + 7): A and B agree on every
-// K, and each lane's codes are two 16-byte loads. The four waves' results
+// K, and each lane's codes are two 16-byte loads. The eight waves' results
 // meet in LDS and are added in wave order.
 
 #include "common.hpp"
@@ -21,9 +24,10 @@ namespace i8h {
 
 namespace {
 
-constexpr int kLnThreads = 256;   // 4 waves
+constexpr int kLnKS = 8;                  // waves, each a share of the K groups
+constexpr int kLnThreads = 64 * kLnKS;
 constexpr int kLnTile = 16;       // output columns and tokens per workgroup
-constexpr int kLnBatch = 4;       // groups a wave loads before it multiplies
+constexpr int kLnBatch = 2;       // groups a wave loads before it multiplies
 
 __device__ __forceinline__ bf16x8 ln_decode(uint32_t lo, uint32_t hi) {
   u32x4 p;
@@ -37,7 +41,7 @@ __device__ __forceinline__ bf16x8 ln_decode(uint32_t lo, uint32_t hi) {
 __global__ void __launch_bounds__(kLnThreads)
 k_linear_i8f16(const uint16_t* __restrict__ x, int T, int K, const int8_t* __restrict__ codes,
                const uint16_t* __restrict__ scales, int N, float* __restrict__ y) {
-  __shared__ f32x4 part[4][kWave];
+  __shared__ f32x4 part[kLnKS][kWave];
   const int n0 = blockIdx.x * kLnTile, t0 = blockIdx.y * kLnTile;
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -50,7 +54,7 @@ k_linear_i8f16(const uint16_t* __restrict__ x, int T, int K, const int8_t* __res
   const uint16_t* srow = scales + (size_t)(n0 + c) * G;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int g0 = wave; g0 < G; g0 += 4 * kLnBatch) {
+  for (int g0 = wave; g0 < G; g0 += kLnKS * kLnBatch) {
     // every load of up to kLnBatch groups is issued before the first product:
     // the codes (the HBM stream), then x (L2-resident) and the scales
     u32x4 cv[kLnBatch][2];
@@ -58,7 +62,7 @@ k_linear_i8f16(const uint16_t* __restrict__ x, int T, int K, const int8_t* __res
     float sc[kLnBatch];
 #pragma unroll
     for (int b = 0; b < kLnBatch; ++b) {
-      const int g = g0 + 4 * b;
+      const int g = g0 + kLnKS * b;
       if (g < G) {
         cv[b][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + (size_t)g * kGroup));
         cv[b][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + (size_t)g * kGroup + 16));
@@ -66,7 +70,7 @@ k_linear_i8f16(const uint16_t* __restrict__ x, int T, int K, const int8_t* __res
     }
 #pragma unroll
     for (int b = 0; b < kLnBatch; ++b) {
-      const int g = g0 + 4 * b;
+      const int g = g0 + kLnKS * b;
       if (g < G) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -77,7 +81,7 @@ k_linear_i8f16(const uint16_t* __restrict__ x, int T, int K, const int8_t* __res
     }
 #pragma unroll
     for (int b = 0; b < kLnBatch; ++b) {
-      const int g = g0 + 4 * b;
+      const int g = g0 + kLnKS * b;
       if (g < G) {
         f32x4 p = {0.f, 0.f, 0.f, 0.f};
         p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[b][0], ln_decode(cv[b][0][0], cv[b][0][1]), p, 0, 0, 0);
@@ -94,7 +98,7 @@ k_linear_i8f16(const uint16_t* __restrict__ x, int T, int K, const int8_t* __res
   if (wave == 0) {
     f32x4 r = part[0][lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
+    for (int w = 1; w < kLnKS; ++w) {
       const f32x4 o = part[w][lane];
 #pragma unroll
       for (int i = 0; i < 4; ++i) r[i] += o[i];
