@@ -82,7 +82,8 @@ const char* i8h_status_string(int status);
  * pair_pos    [P] int32 out
  * workspace   device scratch of at least moe_route_permute_workspace_size()
  *             bytes (may be NULL when that size is 0); contents on entry
- *             are ignored. P must stay below 2^31.
+ *             are ignored. P must stay below 2^31, and ceil(P / 256) * E
+ *             too (else I8H_EUNSUPPORTED).
  * ---------------------------------------------------------------------- */
 size_t moe_route_permute_workspace_size(int T, int E, int topk);
 int moe_route_permute(const float* logits, int T, int E, int topk,

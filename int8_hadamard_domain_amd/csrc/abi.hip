@@ -175,6 +175,8 @@ int moe_route_permute(const float* logits, int T, int E, int topk, int32_t* topk
   if (T < 0 || E <= 0 || topk <= 0) return I8H_EINVAL;
   if (E > kMaxExperts || topk > kMaxTopk || topk > E) return I8H_EUNSUPPORTED;
   if ((int64_t)T * topk >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;
+  // the chunk histograms (256 pairs a chunk, E counts each) are indexed in 32 bits
+  if (((int64_t)T * topk + 255) / 256 * E >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;
   if (T == 0) return I8H_OK;
   if (!logits || !topk_ids || !topk_w || !expert_off || !sorted_pairs || !pair_pos) return I8H_EINVAL;
   if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(expert_off, 4) ||

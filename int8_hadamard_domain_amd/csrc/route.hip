@@ -122,16 +122,40 @@ k_route_scatter(const int32_t* __restrict__ ids, int P, int E, int nchunks,
   __shared__ int wave_tot[4];
   int c = blockIdx.x;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int t = 0, before = 0;
-    for (int cc = 0; cc < nchunks; ++cc) {
-      int h = hist[(size_t)cc * E + e];
-      t += h;
-      if (cc < c) before += h;
-    }
-    tot[e] = t;
-    pre[e] = before;
+    tot[e] = 0;
+    pre[e] = 0;
   }
   for (int i = threadIdx.x; i < 4 * E; i += blockDim.x) wcount[i] = 0;
+  __syncthreads();
+  // tot[e] = sum of hist[cc][e] over all chunks, pre[e] = over chunks before
+  // this one. The block reads the nchunks x E counts together, 16 independent
+  // loads a thread at a time (one chain of loads per expert would cost a
+  // round trip per chunk), and adds them with LDS atomics: integer sums, the
+  // same in any order.
+  const int n = nchunks * E;                          // < 2^31 (the caller checks)
+  const int dcc = kRouteThreads / E, de = kRouteThreads % E;   // (cc, e) step of i += kRouteThreads
+  for (int i0 = threadIdx.x; i0 < n; i0 += 16 * kRouteThreads) {
+    int h[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = i0 + u * kRouteThreads;
+      h[u] = i < n ? hist[i] : 0;
+    }
+    int cc = i0 / E, e = i0 - cc * E;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (h[u] != 0) {
+        atomicAdd(&tot[e], h[u]);
+        if (cc < c) atomicAdd(&pre[e], h[u]);
+      }
+      e += de;
+      cc += dcc;
+      if (e >= E) {  // de < E or de == kRouteThreads < E: one wrap at most
+        e -= E;
+        ++cc;
+      }
+    }
+  }
   __syncthreads();
   block_exclusive_scan(tot, base, E, wave_tot);
   __syncthreads();
@@ -226,6 +250,7 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
   }
   int P = T * k;
   int nchunks = cdiv(P, kChunkPairs);
+  if ((int64_t)nchunks * E >= ((int64_t)1 << 31)) return hipErrorInvalidValue;  // histogram index range
   int32_t* hist = static_cast<int32_t*>(ws);
   k_route_count<<<nchunks, kRouteThreads, 0, st>>>(ids, P, E, hist);
   k_route_scatter<<<nchunks, kRouteThreads, 0, st>>>(ids, P, E, nchunks, hist, expert_off, sorted_pairs,
