@@ -82,6 +82,9 @@ def test_route_validation(L):
     assert route(L, T=100, ws=None) == EINVAL        # workspace needed
     assert route(L, T=100, wsb=16) == EINVAL         # too small
     assert route(L, T=1 << 27, k=16, E=64) == EUNSUP  # P overflows int32
+    # P fits in int32, but ceil(P / 256) * E (the chunk histograms' index) does not
+    assert route(L, T=1 << 24, k=32, E=1024) == EUNSUP
+    assert route(L, T=(1 << 24) - 8, k=32, E=1024, ptr=None) == EINVAL   # just below: other checks apply
 
 
 def rot(L, x=A, ldx=256, y=A, ldy=256, T=4, K=256):
