@@ -217,8 +217,10 @@ __device__ __forceinline__ void prep_x(const XRow<NCH>& X, float (&xv)[NCH][16],
 }
 
 // gate_up (and act) of the wave's RPW row pairs for one token (its prepared
-// activation values xv), stored at sorted row r.
-template <int NCH, int RPW>
+// activation values xv), stored at sorted row r. PIN_SCALES keeps the scale
+// conversions inside the caller's row loop (where the activation row is
+// prepared before the codes arrive, they must not wait for the scale loads).
+template <int NCH, int RPW, bool PIN_SCALES>
 __device__ __forceinline__ void gemv_row(const WaveRows<NCH, RPW>& R, const float (&xv)[NCH][16], int K, int N,
                                          int i0, size_t r, float* __restrict__ gu, float* __restrict__ act,
                                          int lane) {
@@ -233,13 +235,13 @@ __device__ __forceinline__ void gemv_row(const WaveRows<NCH, RPW>& R, const floa
     const int g = min(16 * (lane + kWave * c), K - 16) / kGroup;
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
-      // the codes and scales are loop-invariant over rows; an empty asm keeps
-      // their conversion here (hoisted, it would hold every code as a float,
-      // and the scales' conversion would make the wave wait for their loads
-      // before the activation row is prepared)
+      // the codes (and with PIN_SCALES the scales) are loop-invariant over
+      // rows; an empty asm keeps their conversion here (hoisted, it would hold
+      // every code as a float)
       u32x4 qg = R.cg[j][c], qu = R.cu[j][c];
       uint32_t sg = R.sg[j][c], su = R.su[j][c];
-      asm volatile("" : "+v"(qg), "+v"(qu), "+v"(sg), "+v"(su));
+      asm volatile("" : "+v"(qg), "+v"(qu));
+      if constexpr (PIN_SCALES) asm volatile("" : "+v"(sg), "+v"(su));
       float pg0 = 0.0f, pg1 = 0.0f, pu0 = 0.0f, pu1 = 0.0f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -331,7 +333,7 @@ k_gateup_i8h_gemv(const uint16_t* __restrict__ xin, int K, const int8_t* __restr
       t = sorted_pairs[r + 1] / k;
       load_x(X, xin + (size_t)t * K, K, lane);
     }
-    gemv_row<NCH, RPW>(R, xv, K, N, i0, (size_t)r, gu, act, lane);
+    gemv_row<NCH, RPW, false>(R, xv, K, N, i0, (size_t)r, gu, act, lane);
   }
 }
 
@@ -509,7 +511,7 @@ k_route_gateup_decode(const float* __restrict__ logits, const uint16_t* __restri
     p = rows ? __ffsll((unsigned long long)rows) - 1 : -1;
     rows &= rows - 1;
     if (p >= 0) share.load(x + (size_t)(p / k) * K, K, wave, lane);
-    gemv_row<NCH, RPW>(R, xv, K, N, i0, (size_t)r, gu, act, lane);
+    gemv_row<NCH, RPW, true>(R, xv, K, N, i0, (size_t)r, gu, act, lane);
   }
 }
 
