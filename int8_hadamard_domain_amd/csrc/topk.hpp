@@ -91,27 +91,33 @@ template <int VPL>
 __device__ __forceinline__ void wave_topk_fast(const float (&v)[VPL], int E, int k, int lane, int& id, float& weight,
                                                uint64_t* scratch) {
   constexpr int kGroups = VPL == 1 ? 8 : 4 * VPL;
-  float tau = INFINITY;
+  // the threshold on the order keys (unsigned, monotone in the logit):
+  // integer max and min need no NaN handling between the cross-lane steps;
+  // entries past E take key 0, below every logit's key
+  uint32_t kv[VPL];
+  uint32_t tau = 0xffffffffu;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
-    float m = lane + kWave * i < E ? v[i] : -INFINITY;
-    m = fmaxf(m, xor_lane<1>(m));
-    m = fmaxf(m, xor_lane<2>(m));
-    m = fmaxf(m, xor_lane<4>(m));
-    if constexpr (VPL > 1) m = fmaxf(m, xor_lane<8>(m));
-    tau = fminf(tau, m);
+    kv[i] = lane + kWave * i < E ? order_key(v[i]) : 0u;
+    uint32_t m = kv[i];
+    m = max(m, (uint32_t)xor_lane_i<1>((int)m));
+    m = max(m, (uint32_t)xor_lane_i<2>((int)m));
+    m = max(m, (uint32_t)xor_lane_i<4>((int)m));
+    if constexpr (VPL > 1) m = max(m, (uint32_t)xor_lane_i<8>((int)m));
+    tau = min(tau, m);
   }
-  if constexpr (VPL == 1) tau = fminf(tau, xor_lane<8>(tau));
-  tau = fminf(tau, xor_lane<16>(tau));
-  tau = fminf(tau, xor_lane<32>(tau));
+  if constexpr (VPL == 1) tau = min(tau, (uint32_t)xor_lane_i<8>((int)tau));
+  tau = min(tau, (uint32_t)xor_lane_i<16>((int)tau));
+  tau = min(tau, (uint32_t)xor_lane_i<32>((int)tau));
   uint64_t cm[VPL];
   int C = 0;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
-    cm[i] = __ballot(lane + kWave * i < E && v[i] >= tau);
+    cm[i] = __ballot(kv[i] >= tau && lane + kWave * i < E);
     C += __popcll(cm[i]);
   }
-  if (k > kGroups || C > kWave || !(tau > -INFINITY)) {
+  // a row group with no logit above -inf gives no usable threshold
+  if (k > kGroups || C > kWave || tau <= order_key(-INFINITY)) {
     wave_topk<VPL>(v, E, k, lane, id, weight);
     return;
   }
@@ -122,7 +128,7 @@ __device__ __forceinline__ void wave_topk_fast(const float (&v)[VPL], int E, int
     if ((cm[i] >> lane) & 1) {
       const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(cm[i] >> 32),
                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)cm[i], 0u));
-      scratch[pos] = ((uint64_t)order_key(v[i]) << 8) | (uint64_t)(255 - (lane + kWave * i));
+      scratch[pos] = ((uint64_t)kv[i] << 8) | (uint64_t)(255 - (lane + kWave * i));
     }
     base += __popcll(cm[i]);
   }
