@@ -13,25 +13,12 @@
 
 namespace i8h {
 
-// Wave-wide float maximum (every lane gets it). A maximum needs no exact
-// partner pattern: after the quad steps, rotations by 4 and 8 inside each
-// 16-lane row reach all four quads, then the row and half swaps.
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, xor_lane<1>(v));
-  v = fmaxf(v, xor_lane<2>(v));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
-  v = fmaxf(v, xor_lane<8>(v));
-  v = fmaxf(v, xor_lane<16>(v));
-  v = fmaxf(v, xor_lane<32>(v));
-  return v;
-}
-
 // Top-k of one token by one wave. Lane l holds logits e = l + 64 i. Each
-// round takes the largest open value (a wave maximum) and, among the open
+// round takes the largest open order key (a wave maximum) and, among the open
 // entries equal to it, the lowest expert index (ballots in index order), then
-// retires that entry: the order "larger value first, then lower index".
-// Lane j < k returns the j-th choice and its softmax weight; other lanes
-// return id -1.
+// retires that entry: the order "larger value first, then lower index", with
+// NaN after every number. Lane j < k returns the j-th choice (always an
+// index in [0, E)) and its softmax weight; other lanes return id -1.
 template <int VPL>
 __device__ __forceinline__ void load_logits(const float* __restrict__ row, int E, int lane, float (&v)[VPL]) {
 #pragma unroll
@@ -42,38 +29,63 @@ __device__ __forceinline__ void load_logits(const float* __restrict__ row, int E
 }
 
 // Order-preserving map of a float32 to an unsigned key (+0 and -0 map alike).
+// Every NaN maps to 0, below the key of -inf (0x007fffff): a NaN logit ranks
+// after every number, and NaNs among themselves by index like any tie. No
+// real logit has key 0, so key_logit(0) gives a NaN back.
 __device__ __forceinline__ uint32_t order_key(float v) {
   const uint32_t b = __float_as_uint(v + 0.0f);    // -0 + 0 = +0
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  const uint32_t k = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return v == v ? k : 0u;
+}
+
+// Inverse of order_key on the keys of numbers; key 0 (a NaN) gives a NaN.
+__device__ __forceinline__ float key_logit(uint32_t key) {
+  if (key == 0u) return __uint_as_float(0x7fc00000u);
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
 template <int VPL>
 __device__ __forceinline__ void wave_topk(const float (&v)[VPL], int E, int k, int lane, int& id, float& weight) {
-  uint32_t open = 0;  // bit i: v[i] is a logit not yet taken
+  // ranks the order keys: integer maxima need no NaN handling, and a NaN
+  // (key 0) still takes part, after every number. Entries past E are never
+  // open, and k <= E, so every round finds an open entry.
+  uint32_t kv[VPL];
+  uint32_t open = 0;  // bit i: entry i of this lane not yet taken
 #pragma unroll
-  for (int i = 0; i < VPL; ++i)
+  for (int i = 0; i < VPL; ++i) {
+    kv[i] = order_key(v[i]);
     if (lane + kWave * i < E) open |= 1u << i;
-  int my_id = -1;
-  float my_logit = 0.0f;
+  }
+  int my_id = 0;
+  uint32_t my_key = 0;
   for (int j = 0; j < k; ++j) {
-    float m = -INFINITY;
+    uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
-      if ((open >> i) & 1u) m = fmaxf(m, v[i]);
-    m = wave_max(m);
+      if ((open >> i) & 1u) m = max(m, kv[i]);
+    m = max(m, (uint32_t)xor_lane_i<1>((int)m));
+    m = max(m, (uint32_t)xor_lane_i<2>((int)m));
+    m = max(m, (uint32_t)xor_lane_i<4>((int)m));
+    m = max(m, (uint32_t)xor_lane_i<8>((int)m));
+    m = max(m, (uint32_t)xor_lane_i<16>((int)m));
+    m = max(m, (uint32_t)xor_lane_i<32>((int)m));
     int best = -1;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-      const uint64_t b = __ballot(((open >> i) & 1u) && v[i] == m);
+      const uint64_t b = __ballot(((open >> i) & 1u) && kv[i] == m);
       if (best < 0 && b != 0) best = kWave * i + __ffsll((unsigned long long)b) - 1;
     }
     if ((best % kWave) == lane) open &= ~(1u << (best / kWave));
-    if (lane == j) { my_id = best; my_logit = m; }
+    if (lane == j) {
+      my_id = best;
+      my_key = m;
+    }
   }
+  const float my_logit = key_logit(my_key);
   const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_logit), 0));
   float ex = lane < k ? expf(my_logit - l0) : 0.0f;
   float sum = wave_sum(ex);
-  id = my_id;
+  id = lane < k ? my_id : -1;
   weight = lane < k ? ex / sum : 0.0f;
 }
 
@@ -86,7 +98,8 @@ __device__ __forceinline__ void wave_topk(const float (&v)[VPL], int E, int k, i
 // keys (order key << 8 | 255 - index: larger value first, then lower index),
 // each ranked by counting the keys above it, and the first k are taken in
 // rank order. More than 64 candidates, k above the number of groups, or a
-// NaN or -inf tau fall back to wave_topk. Same ids and weights as wave_topk.
+// tau at or below the key of -inf (a row group of NaNs or -inf only) fall
+// back to wave_topk. Same ids and weights as wave_topk.
 template <int VPL>
 __device__ __forceinline__ void wave_topk_fast(const float (&v)[VPL], int E, int k, int lane, int& id, float& weight,
                                                uint64_t* scratch) {
@@ -145,7 +158,7 @@ __device__ __forceinline__ void wave_topk_fast(const float (&v)[VPL], int E, int
     const uint64_t t = scratch[kWave + lane];
     const uint32_t key = (uint32_t)(t >> 8);
     my_id = 255 - (int)(t & 0xffu);
-    my_logit = __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+    my_logit = key_logit(key);
   }
   const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_logit), 0));
   float ex = lane < k ? expf(my_logit - l0) : 0.0f;

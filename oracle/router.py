@@ -5,6 +5,9 @@ bf16 router; the cards give neither the top-k rule nor the permutation, so
 the readings are:
   * each token t takes the k experts of largest logit, ties going to the
     lower expert index; slot j of token t is the j-th in that order;
+  * a NaN logit ranks after every number (-inf included), NaNs among
+    themselves by index like any tie, so the ids are always valid experts;
+    a token whose chosen logits hold a NaN gets NaN weights;
   * its weights are the softmax over those k logits only (no further
     renormalisation);
   * pair p = t * k + j; experts own contiguous runs of an expert-sorted list
@@ -23,7 +26,8 @@ def topk(logits, k):
     w = np.zeros((t_count, k), dtype=np.float64)
     experts = np.arange(e_count)
     for t in range(t_count):
-        # primary key: larger logit first; secondary: lower expert index
+        # primary key: larger logit first (NaN last); secondary: lower
+        # expert index. NumPy's sorts place NaN after every number.
         order = np.lexsort((experts, -lg[t]))
         sel = order[:k]
         ids[t] = sel

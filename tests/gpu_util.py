@@ -28,6 +28,18 @@ def assert_close(gpu, ref, what, rtol=RTOL, atol=ATOL):
                              f"gpu={gpu[tuple(idx[0])]!r} ref={ref[tuple(idx[0])]!r}")
 
 
+def assert_close_nan(gpu, ref, what, rtol=RTOL, atol=ATOL):
+    """assert_close where NaN is expected: NaN exactly where the oracle has
+    NaN, the other values within the tolerance."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(gpu), nan), f"{what}: NaN positions differ"
+    if (~nan).any():
+        assert_close(gpu[~nan], ref[~nan], what, rtol, atol)
+
+
 def cuda(a, dtype=None):
     t = torch.from_numpy(np.ascontiguousarray(a))
     if dtype is not None:

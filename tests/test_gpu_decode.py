@@ -16,7 +16,7 @@ import torch
 import int8_hadamard_domain_amd as i8h
 import synth
 from oracle import router
-from tests.gpu_util import assert_close, bf16_cuda, check_with_rotation_slack
+from tests.gpu_util import assert_close, assert_close_nan, bf16_cuda, check_with_rotation_slack
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,7 @@ def _run(L, lg=None, what=""):
         got = ro[key].cpu().numpy()
         want = r["ids" if key == "topk_ids" else key]
         assert np.array_equal(got, want.reshape(got.shape)), key
-    assert_close(ro["topk_w"].cpu().numpy(), r["weights"], "topk_w")
+    assert_close_nan(ro["topk_w"].cpu().numpy(), r["weights"], "topk_w")
     check_with_rotation_slack(synth.bf16_bits_to_f64(xb), codes, sbits, r, L.topk, gu, act)
     # the two-call path runs the same arithmetic
     ro2 = i8h.moe_route_permute(d_lg, L.topk)
@@ -89,7 +89,8 @@ def test_logit_ties(gpu_available):
     _run(L, lg=lg.astype(np.float32), what="ties")
 
 
-@pytest.mark.parametrize("case", ["rounded", "fully_tied", "signed_zeros", "top_block_tied", "minus_inf"])
+@pytest.mark.parametrize("case", ["rounded", "fully_tied", "signed_zeros", "top_block_tied", "minus_inf",
+                                  "all_nan", "some_nan", "nan_and_minus_inf"])
 def test_one_token_ties(gpu_available, case):
     # one token: the threshold/candidate top-k and its exact fallback (more
     # than 64 candidates, or a -inf threshold) against the oracle's order
@@ -105,9 +106,26 @@ def test_one_token_ties(gpu_available, case):
         lg[0, 77] = 1.0
     elif case == "top_block_tied":
         lg[0, [3, 90, 17, 64, 120]] = 9.0
-    else:
+    elif case == "minus_inf":
         lg[0, :100] = -np.inf
+    elif case == "all_nan":
+        lg[:] = np.nan
+    elif case == "some_nan":
+        lg[0, ::3] = np.nan                    # NaN in every row group, the rest ranked as usual
+    else:
+        lg[0, :120] = np.nan
+        lg[0, 120:] = -np.inf
     _run(L, lg=lg.astype(np.float32), what=f"one token {case}")
+
+
+def test_nan_logits_several_tokens(gpu_available):
+    # a few tokens in one launch, NaN rows among them: every id a valid
+    # expert, the same grouping as the oracle
+    L = synth.layer("verify", T=4, K=512, E=96, topk=6, N=256, bias_std=0.0)
+    lg = synth.router_logits(L).copy()
+    lg[1] = np.nan
+    lg[2, ::2] = np.nan
+    _run(L, lg=lg.astype(np.float32), what="nan rows")
 
 
 def test_one_token_many_rows(gpu_available):

@@ -14,12 +14,12 @@ import torch
 import int8_hadamard_domain_amd as i8h
 import synth
 from oracle import router
-from tests.gpu_util import assert_close
+from tests.gpu_util import assert_close, assert_close_nan
 
 pytestmark = pytest.mark.gpu
 
 
-def _run_and_compare(lg, k):
+def _run_and_compare(lg, k, nan_weights=False):
     print(f"route T={lg.shape[0]} E={lg.shape[1]} k={k}", flush=True)
     ref = router.route(lg, k)
     out = i8h.moe_route_permute(torch.from_numpy(lg).cuda(), k)
@@ -28,7 +28,10 @@ def _run_and_compare(lg, k):
         got = out[key].cpu().numpy()
         want = ref["ids" if key == "topk_ids" else key]
         assert np.array_equal(got, want.reshape(got.shape)), key
-    assert_close(out["topk_w"].cpu().numpy(), ref["weights"], "topk_w")
+    if nan_weights:
+        assert_close_nan(out["topk_w"].cpu().numpy(), ref["weights"], "topk_w")
+    else:
+        assert_close(out["topk_w"].cpu().numpy(), ref["weights"], "topk_w")
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "verify", "prefill", "fp8"])
@@ -60,3 +63,22 @@ def test_skew_all_to_one_expert(gpu_available):
     lg[:, 5] = 10.0
     lg[:, 9] = 5.0
     _run_and_compare(lg, 2)
+
+
+@pytest.mark.parametrize("T", [3, 40])
+def test_nan_logits(gpu_available, T):
+    # NaN ranks after every number (-inf included), NaNs by index: ids stay
+    # valid experts, so nothing downstream indexes out of range. T = 3 takes
+    # the single-block path, T = 40 the three-kernel path.
+    rng = np.random.default_rng(31 + T)
+    E, k = 128, 8
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    lg[0] = np.nan                                  # a row of NaNs only
+    lg[1, rng.choice(E, 20, replace=False)] = np.nan
+    lg[1, [3, 50]] = 9.0                            # large values beside NaNs
+    lg[2, :64] = -np.inf
+    lg[2, 64:] = np.nan                             # -inf before NaN
+    if T > 3:
+        lg[3:, ::5] = np.nan                        # NaNs in every row
+        lg[5, :] = np.nan
+    _run_and_compare(lg, k, nan_weights=True)

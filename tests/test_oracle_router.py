@@ -43,6 +43,33 @@ def test_topk_matches_sorted_brute_force_with_ties():
     assert np.array_equal(ids[3], np.arange(5))
 
 
+def test_nan_logits_rank_last_by_index():
+    # NaN after every number, -inf included; NaNs among themselves by index
+    rng = np.random.default_rng(23)
+    lg = rng.standard_normal((6, 12)).astype(np.float32)
+    lg[0, [2, 5, 7]] = np.nan
+    lg[1] = np.nan
+    lg[2, :6] = -np.inf
+    lg[2, 6:] = np.nan
+    lg[3, [0, 11]] = np.nan
+    lg[3, 4] = np.inf
+    lg[4, ::2] = np.nan
+    lg[4, 1::2] = -np.inf
+    for k in (1, 4, 12):
+        ids, w = router.topk(lg, k)
+        want = []
+        for t in range(lg.shape[0]):
+            key = lambda e: (1 if np.isnan(lg[t, e]) else 0, 0.0 if np.isnan(lg[t, e]) else -float(lg[t, e]), e)
+            want.append(sorted(range(lg.shape[1]), key=key)[:k])
+        assert np.array_equal(ids, np.array(want))
+        assert np.all((ids >= 0) & (ids < lg.shape[1]))
+        sel = np.take_along_axis(lg, ids, 1)
+        has_nan = np.isnan(sel).any(axis=1)
+        assert np.all(np.isnan(w[has_nan])) and np.all(np.isfinite(w[~has_nan & np.isfinite(sel).all(axis=1)]))
+    assert list(router.topk(lg, 3)[0][1]) == [0, 1, 2]          # all NaN: the lowest indices
+    assert list(router.topk(lg, 8)[0][2]) == [0, 1, 2, 3, 4, 5, 6, 7]  # -inf before NaN
+
+
 def test_negative_zero_ties_positive_zero():
     lg = np.zeros((1, 4), dtype=np.float32)
     lg[0, 0] = -0.0
