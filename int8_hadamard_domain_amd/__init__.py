@@ -89,18 +89,50 @@ def _check(fn, status):
         raise I8HError(fn, status)
 
 
-def _dev(t, name, dtype, ndim=None):
+def _dev(t, name, dtype, ndim=None, shape=None, device=None):
+    """Check one tensor handed to the library: a torch.Tensor on the GPU (on
+    `device` when given), of `dtype`, contiguous, with `ndim` dimensions or
+    exactly `shape`. Raises TypeError / ValueError before anything is launched."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device} (got {t.device})")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions (got {t.dim()})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
+
+
+def _workspace(ws, name, need, device):
+    """A caller's byte workspace (uint8, 1-D, at least `need` bytes, on
+    `device`), or a new one when ws is None."""
+    if ws is None:
+        return torch.empty((max(need, 1),), dtype=torch.uint8, device=device)
+    _dev(ws, name, torch.uint8, 1, device=device)
+    if ws.numel() < need:
+        raise ValueError(f"{name} must hold at least {need} bytes (got {ws.numel()})")
+    return ws
+
+
+def _routing_outputs(out, T, E, topk, device):
+    """The five routing tensors (from `out` where given, checked, else new)."""
+    o = dict(out or {})
+    i32, f32 = torch.int32, torch.float32
+    want = {"topk_ids": (i32, (T, topk)), "topk_w": (f32, (T, topk)), "expert_off": (i32, (E + 1,)),
+            "sorted_pairs": (i32, (T * topk,)), "pair_pos": (i32, (T * topk,))}
+    for key, (dt, shape) in want.items():
+        if key in o:
+            _dev(o[key], key, dt, shape=shape, device=device)
+        else:
+            o[key] = torch.empty(shape, dtype=dt, device=device)
+    return o
 
 
 def _ptr(t):
@@ -119,16 +151,9 @@ def moe_route_permute(logits, topk, out=None):
     _dev(logits, "logits", torch.float32, 2)
     T, E = logits.shape
     dev = logits.device
-    o = dict(out or {})
-    i32 = dict(dtype=torch.int32, device=dev)
-    o.setdefault("topk_ids", torch.empty((T, topk), **i32))
-    o.setdefault("topk_w", torch.empty((T, topk), dtype=torch.float32, device=dev))
-    o.setdefault("expert_off", torch.empty((E + 1,), **i32))
-    o.setdefault("sorted_pairs", torch.empty((T * topk,), **i32))
-    o.setdefault("pair_pos", torch.empty((T * topk,), **i32))
+    o = _routing_outputs(out, T, E, topk, dev)
     ws_bytes = lib().moe_route_permute_workspace_size(T, E, topk)
-    if "workspace" not in o or o["workspace"].numel() < ws_bytes:
-        o["workspace"] = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    o["workspace"] = _workspace(o.get("workspace"), "workspace", ws_bytes, dev)
     _check("moe_route_permute", lib().moe_route_permute(
         _ptr(logits), T, E, topk, _ptr(o["topk_ids"]), _ptr(o["topk_w"]), _ptr(o["expert_off"]),
         _ptr(o["sorted_pairs"]), _ptr(o["pair_pos"]), _ptr(o["workspace"]), o["workspace"].numel(),
@@ -141,7 +166,7 @@ def hadamard128_rotate(x, out=None):
     `out` may be x itself (in place)."""
     _dev(x, "x", torch.bfloat16, 2)
     T, K = x.shape
-    y = torch.empty_like(x) if out is None else _dev(out, "out", torch.bfloat16, 2)
+    y = torch.empty_like(x) if out is None else _dev(out, "out", torch.bfloat16, shape=(T, K), device=x.device)
     _check("hadamard128_rotate", lib().hadamard128_rotate(
         _ptr(x), K, _ptr(y), y.shape[1], T, K, _stream(x.device)))
     return y
@@ -158,16 +183,14 @@ def moe_gateup_i8h_grouped(x_rot, codes, scales, topk, expert_off, sorted_pairs,
     row order (None for skipped outputs).
     """
     _dev(x_rot, "x_rot", torch.bfloat16, 2)
-    _dev(codes, "codes", torch.int8, 3)
-    _dev(scales, "scales", torch.bfloat16, 3)
-    _dev(expert_off, "expert_off", torch.int32, 1)
-    _dev(sorted_pairs, "sorted_pairs", torch.int32, 1)
     T, K = x_rot.shape
-    E, N, K2 = codes.shape
-    if K2 != K or scales.shape != (E, N, K // 128) or expert_off.numel() != E + 1 \
-            or sorted_pairs.numel() != T * topk:
-        raise ValueError("inconsistent shapes")
     dev = x_rot.device
+    _dev(codes, "codes", torch.int8, 3, device=dev)
+    E, N, _ = codes.shape
+    _dev(codes, "codes", torch.int8, shape=(E, N, K))
+    _dev(scales, "scales", torch.bfloat16, shape=(E, N, K // 128), device=dev)
+    _dev(expert_off, "expert_off", torch.int32, shape=(E + 1,), device=dev)
+    _dev(sorted_pairs, "sorted_pairs", torch.int32, shape=(T * topk,), device=dev)
     gu = _out(gate_up, (T * topk, N), dev)
     ac = _out(act, (T * topk, N // 2), dev)
     _check("moe_gateup_i8h_grouped", lib().moe_gateup_i8h_grouped_path(
@@ -182,25 +205,22 @@ def moe_gateup_i8h_grouped_fused(x, codes, scales, topk, expert_off, sorted_pair
     128-wide Hadamard rotation is applied inside the call. Returns
     (gate_up, act)."""
     _dev(x, "x", torch.bfloat16, 2)
-    _dev(codes, "codes", torch.int8, 3)
-    _dev(scales, "scales", torch.bfloat16, 3)
-    _dev(expert_off, "expert_off", torch.int32, 1)
-    _dev(sorted_pairs, "sorted_pairs", torch.int32, 1)
     T, K = x.shape
-    E, N, K2 = codes.shape
-    if K2 != K or scales.shape != (E, N, K // 128) or expert_off.numel() != E + 1 \
-            or sorted_pairs.numel() != T * topk:
-        raise ValueError("inconsistent shapes")
     dev = x.device
+    _dev(codes, "codes", torch.int8, 3, device=dev)
+    E, N, _ = codes.shape
+    _dev(codes, "codes", torch.int8, shape=(E, N, K))
+    _dev(scales, "scales", torch.bfloat16, shape=(E, N, K // 128), device=dev)
+    _dev(expert_off, "expert_off", torch.int32, shape=(E + 1,), device=dev)
+    _dev(sorted_pairs, "sorted_pairs", torch.int32, shape=(T * topk,), device=dev)
     need = lib().moe_gateup_i8h_fused_workspace_size(T, K)
-    if need > 0 and (workspace is None or workspace.numel() < need):
-        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    if need > 0 or workspace is not None:
+        workspace = _workspace(workspace, "workspace", need, dev)
     gu = _out(gate_up, (T * topk, N), dev)
     ac = _out(act, (T * topk, N // 2), dev)
     _check("moe_gateup_i8h_grouped_fused", lib().moe_gateup_i8h_grouped_fused(
         _ptr(x), T, K, _ptr(codes), _ptr(scales), E, N, topk, _ptr(expert_off), _ptr(sorted_pairs),
-        _ptr(gu), _ptr(ac), _ptr(workspace) if need > 0 else None, 0 if workspace is None else workspace.numel(),
-        _stream(dev)))
+        _ptr(gu), _ptr(ac), _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev)))
     return gu, ac
 
 
@@ -210,22 +230,16 @@ def moe_route_gateup_i8h_decode(logits, x, codes, scales, topk, gate_up=True, ac
     E <= 256, K <= 4096). Returns (routing dict as moe_route_permute's,
     gate_up, act). `out` may hold preallocated routing tensors."""
     _dev(logits, "logits", torch.float32, 2)
-    _dev(x, "x", torch.bfloat16, 2)
-    _dev(codes, "codes", torch.int8, 3)
-    _dev(scales, "scales", torch.bfloat16, 3)
     T, E = logits.shape
-    T2, K = x.shape
-    E2, N, K2 = codes.shape
-    if T2 != T or E2 != E or K2 != K or scales.shape != (E, N, K // 128):
-        raise ValueError("inconsistent shapes")
-    dev = x.device
-    o = dict(out or {})
-    i32 = dict(dtype=torch.int32, device=dev)
-    o.setdefault("topk_ids", torch.empty((T, topk), **i32))
-    o.setdefault("topk_w", torch.empty((T, topk), dtype=torch.float32, device=dev))
-    o.setdefault("expert_off", torch.empty((E + 1,), **i32))
-    o.setdefault("sorted_pairs", torch.empty((T * topk,), **i32))
-    o.setdefault("pair_pos", torch.empty((T * topk,), **i32))
+    dev = logits.device
+    _dev(x, "x", torch.bfloat16, 2, device=dev)
+    K = x.shape[1]
+    _dev(x, "x", torch.bfloat16, shape=(T, K))
+    _dev(codes, "codes", torch.int8, 3, device=dev)
+    N = codes.shape[1]
+    _dev(codes, "codes", torch.int8, shape=(E, N, K))
+    _dev(scales, "scales", torch.bfloat16, shape=(E, N, K // 128), device=dev)
+    o = _routing_outputs(out, T, E, topk, dev)
     gu = _out(gate_up, (T * topk, N), dev)
     ac = _out(act, (T * topk, N // 2), dev)
     _check("moe_route_gateup_i8h_decode", lib().moe_route_gateup_i8h_decode(
@@ -240,18 +254,18 @@ def _out(spec, shape, dev):
         return None
     if spec is True:
         return torch.empty(shape, dtype=torch.float32, device=dev)
-    _dev(spec, "output", torch.float32)
-    if tuple(spec.shape) != tuple(shape):
-        raise ValueError(f"output must have shape {shape}")
-    return spec
+    return _dev(spec, "output", torch.float32, shape=shape, device=dev)
 
 
 def fp8_quantize_activations(x, qx=None, sx=None):
     """bf16 [T, K] -> (E4M3 codes uint8 [T, K], float32 scales [T, K/128])."""
     _dev(x, "x", torch.bfloat16, 2)
     T, K = x.shape
-    qx = torch.empty((T, K), dtype=torch.uint8, device=x.device) if qx is None else qx
-    sx = torch.empty((T, K // 128), dtype=torch.float32, device=x.device) if sx is None else sx
+    dev = x.device
+    qx = (torch.empty((T, K), dtype=torch.uint8, device=dev) if qx is None
+          else _dev(qx, "qx", torch.uint8, shape=(T, K), device=dev))
+    sx = (torch.empty((T, K // 128), dtype=torch.float32, device=dev) if sx is None
+          else _dev(sx, "sx", torch.float32, shape=(T, K // 128), device=dev))
     _check("fp8_quantize_activations", lib().fp8_quantize_activations(
         _ptr(x), T, K, _ptr(qx), _ptr(sx), _stream(x.device)))
     return qx, sx
@@ -267,19 +281,16 @@ def moe_gateup_fp8blk_grouped(x, codes, scales, topk, expert_off, sorted_pairs,
     (see fp8_workspace_views).
     """
     _dev(x, "x", torch.bfloat16, 2)
-    _dev(codes, "codes", torch.uint8, 3)
-    _dev(scales, "scales", torch.bfloat16, 3)
-    _dev(expert_off, "expert_off", torch.int32, 1)
-    _dev(sorted_pairs, "sorted_pairs", torch.int32, 1)
     T, K = x.shape
-    E, N, K2 = codes.shape
-    if K2 != K or scales.shape != (E, N // 128, K // 128) or expert_off.numel() != E + 1 \
-            or sorted_pairs.numel() != T * topk:
-        raise ValueError("inconsistent shapes")
     dev = x.device
+    _dev(codes, "codes", torch.uint8, 3, device=dev)
+    E, N, _ = codes.shape
+    _dev(codes, "codes", torch.uint8, shape=(E, N, K))
+    _dev(scales, "scales", torch.bfloat16, shape=(E, N // 128, K // 128), device=dev)
+    _dev(expert_off, "expert_off", torch.int32, shape=(E + 1,), device=dev)
+    _dev(sorted_pairs, "sorted_pairs", torch.int32, shape=(T * topk,), device=dev)
     need = lib().moe_gateup_fp8blk_workspace_size(T, K)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, "workspace", need, dev)
     gu = _out(gate_up, (T * topk, N), dev)
     ac = _out(act, (T * topk, N // 2), dev)
     _check("moe_gateup_fp8blk_grouped", lib().moe_gateup_fp8blk_grouped_path(
@@ -309,26 +320,25 @@ def moe_down_bf16_combine(act, w_down, routing, out=None, workspace=None, path="
     pair_pos); `path` is "auto", "gemv" (one launch) or "gemm" (GEMM +
     combine)."""
     _dev(act, "act", torch.float32, 2)
-    _dev(w_down, "w_down", torch.bfloat16, 3)
-    ids = _dev(routing["topk_ids"], "topk_ids", torch.int32, 2)
-    tw = _dev(routing["topk_w"], "topk_w", torch.float32, 2)
-    off = _dev(routing["expert_off"], "expert_off", torch.int32, 1)
-    pos = _dev(routing["pair_pos"], "pair_pos", torch.int32, 1)
-    T, topk = ids.shape
     P, I = act.shape
-    E, H, I2 = w_down.shape
-    if I2 != I or P != T * topk or tw.shape != ids.shape or off.numel() != E + 1 or pos.numel() != P:
-        raise ValueError("inconsistent shapes")
     dev = act.device
+    _dev(w_down, "w_down", torch.bfloat16, 3, device=dev)
+    E, H, _ = w_down.shape
+    _dev(w_down, "w_down", torch.bfloat16, shape=(E, H, I))
+    ids = _dev(routing["topk_ids"], "topk_ids", torch.int32, 2, device=dev)
+    T, topk = ids.shape
+    if P != T * topk:
+        raise ValueError(f"act must have T * topk = {T * topk} rows (got {P})")
+    tw = _dev(routing["topk_w"], "topk_w", torch.float32, shape=(T, topk), device=dev)
+    off = _dev(routing["expert_off"], "expert_off", torch.int32, shape=(E + 1,), device=dev)
+    pos = _dev(routing["pair_pos"], "pair_pos", torch.int32, shape=(P,), device=dev)
     need = lib().moe_down_bf16_workspace_size(T, I, H, topk)
-    if path != "gemv" and need > 0 and (workspace is None or workspace.numel() < need):
-        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    if path != "gemv" or workspace is not None:
+        workspace = _workspace(workspace, "workspace", need, dev)
     if out is None:
         out = torch.empty((T, H), dtype=torch.float32, device=dev)
     else:
-        _dev(out, "out", torch.float32, 2)
-        if tuple(out.shape) != (T, H):
-            raise ValueError(f"out must have shape {(T, H)}")
+        _dev(out, "out", torch.float32, shape=(T, H), device=dev)
     _check("moe_down_bf16_combine", lib().moe_down_bf16_combine_path(
         _ptr(act), T, I, _ptr(w_down), E, H, topk, _ptr(ids), _ptr(tw), _ptr(off), _ptr(pos), _ptr(out),
         _ptr(workspace), 0 if workspace is None else workspace.numel(), DOWN_PATHS[path], _stream(dev)))
@@ -339,19 +349,16 @@ def linear_i8f16(x, codes, scales, out=None):
     """Dense int8 linear: x [T, K] bf16 (unrotated), codes [N, K] int8,
     scales [N, K/128] float16 -> y [T, N] float32."""
     _dev(x, "x", torch.bfloat16, 2)
-    _dev(codes, "codes", torch.int8, 2)
-    _dev(scales, "scales", torch.float16, 2)
     T, K = x.shape
-    N, K2 = codes.shape
-    if K2 != K or tuple(scales.shape) != (N, K // 128):
-        raise ValueError("inconsistent shapes")
     dev = x.device
+    _dev(codes, "codes", torch.int8, 2, device=dev)
+    N = codes.shape[0]
+    _dev(codes, "codes", torch.int8, shape=(N, K))
+    _dev(scales, "scales", torch.float16, shape=(N, K // 128), device=dev)
     if out is None:
         out = torch.empty((T, N), dtype=torch.float32, device=dev)
     else:
-        _dev(out, "out", torch.float32, 2)
-        if tuple(out.shape) != (T, N):
-            raise ValueError(f"out must have shape {(T, N)}")
+        _dev(out, "out", torch.float32, shape=(T, N), device=dev)
     _check("linear_i8f16", lib().linear_i8f16(_ptr(x), T, K, _ptr(codes), _ptr(scales), N, _ptr(out), _stream(dev)))
     return out
 
@@ -376,19 +383,16 @@ def moe_gateup_i8g_grouped(x, codes, scales, topk, expert_off, sorted_pairs,
     activations and their scales (see i8g_workspace_views).
     """
     _dev(x, "x", torch.bfloat16, 2)
-    _dev(codes, "codes", torch.int8, 3)
-    _dev(scales, "scales", torch.bfloat16, 3)
-    _dev(expert_off, "expert_off", torch.int32, 1)
-    _dev(sorted_pairs, "sorted_pairs", torch.int32, 1)
     T, K = x.shape
-    E, N, K2 = codes.shape
-    if K2 != K or scales.shape != (E, N, K // 128) or expert_off.numel() != E + 1 \
-            or sorted_pairs.numel() != T * topk:
-        raise ValueError("inconsistent shapes")
     dev = x.device
+    _dev(codes, "codes", torch.int8, 3, device=dev)
+    E, N, _ = codes.shape
+    _dev(codes, "codes", torch.int8, shape=(E, N, K))
+    _dev(scales, "scales", torch.bfloat16, shape=(E, N, K // 128), device=dev)
+    _dev(expert_off, "expert_off", torch.int32, shape=(E + 1,), device=dev)
+    _dev(sorted_pairs, "sorted_pairs", torch.int32, shape=(T * topk,), device=dev)
     need = lib().moe_gateup_i8g_workspace_size(T, K)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, "workspace", need, dev)
     gu = _out(gate_up, (T * topk, N), dev)
     ac = _out(act, (T * topk, N // 2), dev)
     _check("moe_gateup_i8g_grouped", lib().moe_gateup_i8g_grouped(
