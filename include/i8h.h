@@ -74,7 +74,10 @@ const char* i8h_status_string(int status);
  * lists expert e's pairs in increasing p; pair_pos[p] is the position of p
  * in sorted_pairs. All integer outputs are deterministic, bit for bit.
  *
- * logits      [T, E] float32, finite (NaN or infinity: result unspecified)
+ * logits      [T, E] float32. A NaN ranks after every number (-inf
+ *             included), NaNs among themselves by index like ties, so every
+ *             id is an expert in [0, E); a token whose chosen logits hold a
+ *             NaN (or only -inf) gets NaN weights.
  * topk_ids    [T, topk] int32 out
  * topk_w      [T, topk] float32 out
  * expert_off  [E + 1] int32 out
@@ -126,7 +129,9 @@ int hadamard128_rotate(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy,
  * expert_off  [E + 1], sorted_pairs [T*topk]: as moe_route_permute writes them
  * gate_up     [T*topk, N] float32 out, or NULL to skip storing it
  * act         [T*topk, N/2] float32 out, or NULL to skip storing it
- * N must be a positive multiple of 64 (gate and up halves of 32-row tiles).
+ * N must be positive and even (odd: I8H_EINVAL); the kernels tile the gate
+ * and up halves in 32-row pieces, so an N that is not a multiple of 64 is
+ * I8H_EUNSUPPORTED.
  * ---------------------------------------------------------------------- */
 int moe_gateup_i8h_grouped(const uint16_t* x_rot, int T, int K,
                            const int8_t* codes, const uint16_t* scales,
@@ -144,7 +149,11 @@ int moe_gateup_i8h_grouped(const uint16_t* x_rot, int T, int K,
  * I8H_PATH_SKINNY (bf16 MFMA for few pairs per expert: passes of 64 pairs,
  * units of 64 gate + 64 up columns, two workgroups per CU).
  * All give the same result to float32 rounding. TALL needs N*K < 2^31
- * (else I8H_EUNSUPPORTED). */
+ * (else I8H_EUNSUPPORTED); its running result spans 2^64 of scale range per
+ * row: a group whose scale lies more than 2^64 below the largest scale before
+ * it in the row contributes nothing (its terms are below 2^-64 of that
+ * scale's), which keeps every intermediate finite for activations below 2^46
+ * at K = 2048. */
 enum { I8H_PATH_AUTO = 0, I8H_PATH_GEMV = 1, I8H_PATH_GEMM = 2, I8H_PATH_TALL = 3, I8H_PATH_SKINNY = 4 };
 int moe_gateup_i8h_grouped_path(const uint16_t* x_rot, int T, int K,
                                 const int8_t* codes, const uint16_t* scales,
@@ -178,7 +187,8 @@ int moe_gateup_i8h_grouped_fused(const uint16_t* x, int T, int K,
  * stores the routing outputs. Same inputs, outputs and rules as those two
  * calls (x is the UNROTATED activation), with the same bit-exact routing;
  * no workspace. Limits (else I8H_EUNSUPPORTED): T*topk <= 64, E <= 256,
- * K <= 4096. Needs at least one of gate_up and act; N % 64 == 0. */
+ * K <= 4096. Needs at least one of gate_up and act; N even (odd: I8H_EINVAL)
+ * and a multiple of 64 (else I8H_EUNSUPPORTED). */
 int moe_route_gateup_i8h_decode(const float* logits, const uint16_t* x, int T, int K,
                                 const int8_t* codes, const uint16_t* scales,
                                 int E, int N, int topk,
@@ -322,8 +332,9 @@ int i8_quantize_activations(const uint16_t* x, int T, int K,
  * with the epilogue, row order and outputs of moe_gateup_i8h_grouped. The
  * group sums are exact int32 (int8 MFMA); each is folded into the float32
  * result with sw * sx. codes [E, N, K] int8 in -127..127, 16-B aligned;
- * scales [E, N, K/128] bf16, 4-B aligned; N a positive multiple of 64 and
- * N*K < 2^31 (else I8H_EUNSUPPORTED). Workspace: at least
+ * scales [E, N, K/128] bf16, 4-B aligned; N positive and even (odd:
+ * I8H_EINVAL), a multiple of 64 and N*K < 2^31 (else I8H_EUNSUPPORTED).
+ * Workspace: at least
  * moe_gateup_i8g_workspace_size(T, K) bytes, 256-B aligned: qx [T, K] int8
  * at offset 0, sx [T, K/128] float32 at offset round_up(T*K, 256), left there
  * for the caller. Passes of 192 pairs: one per expert at prefill sizes. */

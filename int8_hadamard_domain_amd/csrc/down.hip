@@ -149,6 +149,12 @@ constexpr int dg_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | 
 // compiler neither counts nor waits on it; the kernel waits with vmcnt.
 // The base goes through readfirstlane: it is uniform, but the compiler does not
 // always prove it, and an "s" operand must be an SGPR.
+// M0 is a register the compiler reserves: it never allocates it, but sets it
+// right before its own instructions that read it. Naming it clobbered orders
+// these statements against such uses; the compiler still warns that it does
+// not preserve reserved registers, which is what is wanted here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dg_dma16(uint32_t off, const void* base, uint32_t lds) {
   // (readfirstlane returns a signed int: take both halves as uint32_t before
   // widening, or a low word with bit 31 set would sign-extend over the high one)
@@ -158,8 +164,9 @@ __device__ __forceinline__ void dg_dma16(uint32_t off, const void* base, uint32_
   const uint64_t u = ((uint64_t)hi << 32) | lo;
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off),
                "s"(reinterpret_cast<const void*>(u)), "s"(lds)
-               : "memory");
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // A row (or B row) of a stage is 64 bytes = 4 pieces of 16; piece p of row r
 // sits at position p ^ ((r >> 2) & 3), so 16 consecutive rows read at one

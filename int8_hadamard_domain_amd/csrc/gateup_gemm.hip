@@ -109,26 +109,34 @@ __shared__ __attribute__((aligned(16))) uint32_t gC3[2 * kGateRows];
 // One 16- or 4-byte copy per lane, global -> LDS (M0 = the wave's LDS base;
 // lane l's bytes land at base + size * l). Issued as inline assembly so that
 // the compiler neither waits on it nor counts it; the kernel waits with
-// explicit s_waitcnt vmcnt. M0 is not used by any other code of the kernel.
+// explicit s_waitcnt vmcnt. Each statement names M0 as clobbered, so the
+// compiler keeps no value of its own in M0 across it.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)p);
 }
+// M0 is a register the compiler reserves: it never allocates it, but sets it
+// right before its own instructions that read it. Naming it clobbered orders
+// these statements against such uses; the compiler still warns that it does
+// not preserve reserved registers, which is what is wanted here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
 // The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
 // byte offset (one VGPR per copy instead of a 64-bit address pair).
 __device__ __forceinline__ void dma16s(uint32_t off, const void* base, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
-               : "memory");
+               : "memory", "m0");
 }
 __device__ __forceinline__ void dma4s(uint32_t off, const void* base, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
-               : "memory");
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // LDS stage layouts. A: 128 rows x 64 bf16 (128 B, 8 pieces of 16 B), piece
 // p of row r at position p ^ ((r >> 1) & 7). B: 256 rows (gate 0..127, up
@@ -363,7 +371,12 @@ k_gateup_gemm(const uint16_t* __restrict__ xa, const float* __restrict__ sx, int
 // element, no second accumulator) and the MFMAs add that group's plain code
 // products P_g on top; the stored value is R * s_last. The ratio adds about
 // two float32 roundings per group. A zero scale keeps the current one and its
-// codes are masked to zero, so such a group contributes exactly nothing.
+// codes are masked to zero, so such a group contributes exactly nothing. So
+// does a group whose scale lies more than 2^64 below the largest one taken
+// before it in the row: that keeps |R| below 2^64 * 127 * K * max|x|, finite
+// for any activation below 2^46 at K = 2048 (a dropped group's terms are
+// below 2^-64 s_max 127 sum|x|; terms more than 2^126 below a later, larger
+// scale underflow the same way).
 // Freed of the second accumulator, each wave holds 4 m-tiles x (32 gate + 32
 // up) columns: every code it decodes feeds four MFMAs, and a prefill-sized
 // expert (up to 256 pairs) is covered in one pass, so its codes are read
@@ -525,8 +538,15 @@ k_gateup_gemm_tall(const uint16_t* __restrict__ xa, int K, const uint8_t* __rest
 #pragma unroll
         for (int j = 0; j < 16; ++j) R[a][c][j] = 0.0f;
     float seff_g = 1.0f, seff_u = 1.0f;  // the scale R is currently expressed in
+    float smax_g = 0.0f, smax_u = 0.0f;  // largest scale taken so far; 0 while R is still exactly 0
     uint32_t mask_g = ~0u, mask_u = ~0u;
     bool need_mask = false;
+    // A group's scale s joins the running result unless it is zero or lies
+    // more than 2^64 below the largest scale taken before it in the row
+    // (then the group is masked like a zero-scale one: its terms are below
+    // 2^-64 of that scale's). This bounds every rescale factor by 2^64, so R
+    // stays finite; nothing is rescaled while R is still exactly 0.
+    auto take = [](float sc, float smax) { return sc != 0.0f && sc >= smax * 0x1p-64f; };
 
     auto body = [&](auto na_c, int h, const uint16_t* abuf, const uint8_t* bbuf, const uint32_t* cbuf)
         __attribute__((always_inline)) {
@@ -540,11 +560,12 @@ k_gateup_gemm_tall(const uint16_t* __restrict__ xa, int K, const uint8_t* __rest
         su = half_bf16(cbuf[cu_idx], (par_u + g) & 1);
       }
       if (h == 0) {
-        if (sg != 0.0f) seff_g = sg;
-        if (su != 0.0f) seff_u = su;
-        mask_g = sg != 0.0f ? ~0u : 0u;
-        mask_u = su != 0.0f ? ~0u : 0u;
-        need_mask = __ballot(sg == 0.0f || su == 0.0f) != 0;
+        const bool tg = sg != 0.0f, tu = su != 0.0f;
+        if (tg) seff_g = smax_g = sg;
+        if (tu) seff_u = smax_u = su;
+        mask_g = tg ? ~0u : 0u;
+        mask_u = tu ? ~0u : 0u;
+        need_mask = __ballot(!tg || !tu) != 0;
       }
       u32x4 cgp[2], cup[2];  // the lane's 32 codes of its gate and up rows in this stage
 #pragma unroll
@@ -577,8 +598,11 @@ k_gateup_gemm_tall(const uint16_t* __restrict__ xa, int K, const uint8_t* __rest
         }
       }
       if (next_c) {
-        // express R in the next group's scale; a zero scale keeps the current one
-        const float rgt = sg != 0.0f ? seff_g / sg : 1.0f, rut = su != 0.0f ? seff_u / su : 1.0f;
+        // express R in the next group's scale; a masked group keeps the
+        // current one (factors within [2^-64, 2^64] once R holds a term)
+        const bool tg = take(sg, smax_g), tu = take(su, smax_u);
+        const float rgt = tg && smax_g != 0.0f ? seff_g / sg : 1.0f;
+        const float rut = tu && smax_u != 0.0f ? seff_u / su : 1.0f;
 #pragma unroll
         for (int a = 0; a < NA; ++a)
 #pragma unroll
@@ -586,11 +610,17 @@ k_gateup_gemm_tall(const uint16_t* __restrict__ xa, int K, const uint8_t* __rest
             R[a][0][j] *= rgt;
             R[a][1][j] *= rut;
           }
-        if (sg != 0.0f) seff_g = sg;
-        if (su != 0.0f) seff_u = su;
-        mask_g = sg != 0.0f ? ~0u : 0u;
-        mask_u = su != 0.0f ? ~0u : 0u;
-        need_mask = __ballot(sg == 0.0f || su == 0.0f) != 0;
+        if (tg) {
+          seff_g = sg;
+          smax_g = fmaxf(smax_g, sg);
+        }
+        if (tu) {
+          seff_u = su;
+          smax_u = fmaxf(smax_u, su);
+        }
+        mask_g = tg ? ~0u : 0u;
+        mask_u = tu ? ~0u : 0u;
+        need_mask = __ballot(!tg || !tu) != 0;
       }
     };
 

@@ -76,18 +76,25 @@ __device__ __forceinline__ const void* g_uniform(const void* p) {
 // one 16- or 4-byte copy per lane, global (uniform base + 32-bit lane offset)
 // -> LDS (M0 = the wave's LDS base; lane l's bytes land at base + size * l);
 // the kernel waits with vmcnt
+// M0 is a register the compiler reserves: it never allocates it, but sets it
+// right before its own instructions that read it. Naming it clobbered orders
+// these statements against such uses; the compiler still warns that it does
+// not preserve reserved registers, which is what is wanted here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void g_dma16(uint32_t off, const void* base, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
-               : "memory");
+               : "memory", "m0");
 }
 __device__ __forceinline__ void g_dma4(uint32_t off, const void* base, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
-               : "memory");
+               : "memory", "m0");
 }
 // the same with a 64-bit per-lane address
 __device__ __forceinline__ void g_dma4v(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 // s_waitcnt vmcnt(0) with expcnt and lgkmcnt unconstrained (gfx9 field layout)
 constexpr int kVmcnt0 = (0x7 << 4) | (0xF << 8);
 

@@ -70,12 +70,19 @@ __device__ __forceinline__ uint32_t s_lds(const void* p) {
 }
 // one 16- or 4-byte copy per lane, global -> LDS (M0 = the wave's LDS base;
 // lane l's bytes land at base + size * l); the kernel waits with vmcnt
+// M0 is a register the compiler reserves: it never allocates it, but sets it
+// right before its own instructions that read it. Naming it clobbered orders
+// these statements against such uses; the compiler still warns that it does
+// not preserve reserved registers, which is what is wanted here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void s_dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
 __device__ __forceinline__ void s_dma4(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 // s_waitcnt vmcnt(n) for a wave-uniform count known at run time (0..10)
 __device__ __forceinline__ void s_wait_dyn(int n) {
   switch (n) {
