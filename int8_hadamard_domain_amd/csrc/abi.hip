@@ -48,7 +48,8 @@ int gateup_i8h(const uint16_t* x_rot, int T, int K, const int8_t* codes, const u
                int path, void* stream) {
   int rc = check_common_moe(T, K, E, N, topk);
   if (rc != I8H_OK) return rc;
-  if ((N % 64) != 0) return I8H_EINVAL;
+  if ((N % 2) != 0) return I8H_EINVAL;                  // gate and up halves
+  if ((N % 64) != 0) return I8H_EUNSUPPORTED;           // 32-row gate and up tiles
   if (path < I8H_PATH_AUTO || path > I8H_PATH_SKINNY) return I8H_EINVAL;
   if (T == 0) return I8H_OK;
   if (!x_rot || !codes || !scales || !expert_off || !sorted_pairs) return I8H_EINVAL;
@@ -242,7 +243,8 @@ int moe_gateup_i8h_grouped_fused(const uint16_t* x, int T, int K, const int8_t* 
                                  void* stream) {
   int rc = check_common_moe(T, K, E, N, topk);
   if (rc != I8H_OK) return rc;
-  if ((N % 64) != 0) return I8H_EINVAL;
+  if ((N % 2) != 0) return I8H_EINVAL;                  // gate and up halves
+  if ((N % 64) != 0) return I8H_EUNSUPPORTED;           // 32-row gate and up tiles
   if (T == 0) return I8H_OK;
   if (!x || !codes || !scales || !expert_off || !sorted_pairs) return I8H_EINVAL;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return I8H_EINVAL;
@@ -270,7 +272,8 @@ int moe_route_gateup_i8h_decode(const float* logits, const uint16_t* x, int T, i
                                 float* act, void* stream) {
   int rc = check_common_moe(T, K, E, N, topk);
   if (rc != I8H_OK) return rc;
-  if ((N % 64) != 0) return I8H_EINVAL;
+  if ((N % 2) != 0) return I8H_EINVAL;                  // gate and up halves
+  if ((N % 64) != 0) return I8H_EUNSUPPORTED;           // 32-row gate and up tiles
   if ((int64_t)T * topk > kDecodeMaxPairs || E > kDecodeMaxExperts || K > kGemvMaxK) return I8H_EUNSUPPORTED;
   if (T == 0) return I8H_OK;
   if (!logits || !x || !codes || !scales || !topk_ids || !topk_w || !expert_off || !sorted_pairs || !pair_pos)
@@ -349,7 +352,8 @@ int moe_gateup_i8g_grouped(const uint16_t* x, int T, int K, const int8_t* codes,
                            float* act, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_common_moe(T, K, E, N, topk);
   if (rc != I8H_OK) return rc;
-  if ((N % 64) != 0) return I8H_EINVAL;
+  if ((N % 2) != 0) return I8H_EINVAL;                  // gate and up halves
+  if ((N % 64) != 0) return I8H_EUNSUPPORTED;           // 32-row gate and up tiles
   if ((int64_t)N * K >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;   // one expert's codes, 32-bit offsets
   if (T == 0) return I8H_OK;
   if (!x || !codes || !scales || !expert_off || !sorted_pairs) return I8H_EINVAL;

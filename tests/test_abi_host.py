@@ -111,7 +111,10 @@ def gemm(L, x=A, T=4, K=256, codes=A, scales=A, E=8, N=256, k=2, off=A, sp=A, gu
 
 def test_gateup_i8h_validation(L):
     assert gemm(L, K=100) == EINVAL
-    assert gemm(L, N=96) == EINVAL                   # N % 64
+    assert gemm(L, N=97) == EINVAL                   # odd N: no gate/up halves
+    assert gemm(L, N=96) == EUNSUP                   # even, but not whole 32-row gate/up tiles
+    assert gemm(L, N=160, path=1) == EUNSUP          # (every path)
+    assert gemm(L, N=2, path=4) == EUNSUP
     assert gemm(L, E=2000) == EUNSUP
     assert gemm(L, k=3, E=2) == EUNSUP
     assert gemm(L, path=7) == EINVAL
@@ -127,6 +130,8 @@ def test_gateup_i8h_validation(L):
 def test_fused_validation(L):
     f = L.moe_gateup_i8h_grouped_fused
     assert f(A, 4, 100, A, A, 8, 256, 2, A, A, A, A, None, 0, None) == EINVAL
+    assert f(A, 4, 256, A, A, 8, 255, 2, A, A, A, A, None, 0, None) == EINVAL    # odd N
+    assert f(A, 4, 256, A, A, 8, 160, 2, A, A, A, A, None, 0, None) == EUNSUP    # even N, not N % 64
     assert f(A, 100, 256, A, A, 8, 256, 2, A, A, A, A, None, 0, None) == EINVAL     # workspace needed
     assert f(A, 100, 256, A, A, 8, 256, 2, A, A, A, A, A, 16, None) == EINVAL       # too small
     assert f(A, 0, 256, A, A, 8, 256, 2, A, A, A, A, None, 0, None) == OK
@@ -159,7 +164,8 @@ def dec(L, lg=A, x=A, T=1, K=2048, codes=A, scales=A, E=128, N=1536, k=8, gu=A, 
 
 def test_decode_validation(L):
     assert dec(L, K=100) == EINVAL
-    assert dec(L, N=96) == EINVAL                    # N % 64
+    assert dec(L, N=95) == EINVAL                    # odd N
+    assert dec(L, N=96) == EUNSUP                    # even N outside the 32-row tiles
     assert dec(L, T=9) == EUNSUP                     # 72 pairs > 64
     assert dec(L, E=257, k=8) == EUNSUP              # more than 4 logits per lane
     assert dec(L, K=8192) == EUNSUP
@@ -210,7 +216,8 @@ def test_linear_validation(L):
 
 def test_i8g_validation(L):
     f = L.moe_gateup_i8g_grouped
-    assert f(A, 4, 256, A, A, 8, 224, 2, A, A, A, A, A, 1 << 20, None) == EINVAL    # N % 64
+    assert f(A, 4, 256, A, A, 8, 225, 2, A, A, A, A, A, 1 << 20, None) == EINVAL    # odd N
+    assert f(A, 4, 256, A, A, 8, 224, 2, A, A, A, A, A, 1 << 20, None) == EUNSUP    # even N, not N % 64
     assert f(A, 4, 200, A, A, 8, 256, 2, A, A, A, A, A, 1 << 20, None) == EINVAL    # K % 128
     assert f(A, 4, 256, A, A, 8, 256, 2, A, A, A, A, None, 1 << 20, None) == EINVAL  # no workspace
     assert f(A, 4, 256, A, A, 8, 256, 2, A, A, A, A, A, 16, None) == EINVAL         # too small

@@ -127,6 +127,39 @@ def test_fp8_blocks_against_torch_cast():
                 assert np.all(np.abs(np.abs(dec) - np.minimum(np.abs(ratio), 448)) <= near + 1e-12)
 
 
+def test_fp8_block_dequantize_brute_force_and_bound():
+    # W_hat[e, n, k] = s[e, n // 128, k // 128] * value of code[e, n, k]: each
+    # element computed one by one, the code's value from torch's own E4M3FN
+    # decoder (independent of the oracle's codec)
+    rng = np.random.default_rng(16)
+    w = rng.standard_normal((2, 256, 384)) * 0.02
+    w[1, :128, 128:256] = 0.0                                # a zero block
+    w[0, 5, 7] = 3.0                                         # a block with one large value
+    codes, scales = quant.quantize_fp8_blocks(w)
+    what = quant.dequantize_fp8_blocks(codes, scales)
+    assert what.shape == w.shape
+    tv = torch.from_numpy(codes.reshape(-1)).view(torch.float8_e4m3fn).to(torch.float64).numpy().reshape(codes.shape)
+    rows = rng.integers(0, 256, 40)
+    cols = rng.integers(0, 384, 40)
+    for e in range(2):
+        for n, k in zip(rows.tolist(), cols.tolist()):
+            assert what[e, n, k] == scales[e, n // 128, k // 128] * float(tv[e, n, k])
+    assert np.array_equal(what, np.repeat(np.repeat(scales, 128, -2), 128, -1) * tv)
+    assert np.all(what[1, :128, 128:256] == 0)
+    # round trip: within half an E4M3 step of w / s (steps: 2^(e - 3) for
+    # normals, 2^-9 below 2^-6), times s; the block maximum itself is exact to
+    # the scale's bf16 rounding (|w / s| lands within one E4M3 step of 448)
+    sb = np.repeat(np.repeat(scales, 128, -2), 128, -1)
+    nz = sb > 0
+    r = np.abs(w[nz] / sb[nz])
+    step = np.where(r >= 2.0 ** -6, np.ldexp(1.0, np.floor(np.log2(np.maximum(r, 2.0 ** -6))).astype(int) - 3),
+                    2.0 ** -9)
+    sat = r > 448
+    err = np.abs(w[nz] - what[nz]) / sb[nz]
+    assert np.all(err[~sat] <= step[~sat] / 2 * (1 + 1e-12))
+    assert np.all(err[sat] <= r[sat] - 448 + 1e-12)
+
+
 def test_fp8_zero_block():
     w = np.zeros((128, 128))
     codes, scales = quant.quantize_fp8_blocks(w)
