@@ -94,6 +94,24 @@ int moe_route_permute(const float* logits, int T, int E, int topk,
                       int32_t* sorted_pairs, int32_t* pair_pos,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_route_permute without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same inputs, outputs, rules and results,
+ * bit for bit. The call allocates nothing: the histograms that the workspace
+ * holds otherwise live in a fixed 1 MiB device array inside the library, one
+ * per GPU, held until the process ends; so ceil(T*topk / 256) * E * 4 bytes
+ * (moe_route_permute_workspace_size) must not exceed 1 MiB (else
+ * I8H_EUNSUPPORTED; e.g. T*topk <= 524,288 pairs at E = 128). The array's
+ * device address is looked up on the first call on each device: the stream
+ * must belong to the current device (else I8H_EHIP). Every call on one GPU
+ * shares that array: calls that overlap on one GPU (on different streams, or
+ * from several threads) race on it and give unspecified results; calls one
+ * after another on a stream are safe (nothing in the array must start at
+ * zero). */
+int moe_route_permute_noalloc(const float* logits, int T, int E, int topk,
+                              int32_t* topk_ids, float* topk_w, int32_t* expert_off,
+                              int32_t* sorted_pairs, int32_t* pair_pos, void* stream);
+
 /* ------------------------------------------------------------------------
  * Blockwise 128-wide Walsh-Hadamard rotation of bf16 activation rows.
  *

@@ -8,6 +8,7 @@ the library is not built, or a tensor is not on the GPU, the call raises.
 
 Functions (same names as the C entry points):
   moe_route_permute          top-k routing and the expert-sorted permutation
+  moe_route_permute_noalloc  the same without a workspace (fixed device scratch)
   hadamard128_rotate         blockwise 128-wide Walsh-Hadamard rotation (bf16)
   moe_gateup_i8h_grouped     grouped int8 Hadamard-domain gate_up + GELU epilogue
   moe_gateup_i8h_grouped_fused  the same on unrotated activations (rotation fused)
@@ -58,6 +59,7 @@ def lib():
         "i8h_status_string": (ctypes.c_char_p, [I]),
         "moe_route_permute_workspace_size": (SZ, [I, I, I]),
         "moe_route_permute": (I, [P, I, I, I, P, P, P, P, P, P, SZ, P]),
+        "moe_route_permute_noalloc": (I, [P, I, I, I, P, P, P, P, P, P]),
         "hadamard128_rotate": (I, [P, I64, P, I64, I, I, P]),
         "moe_gateup_i8h_grouped": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P]),
         "moe_gateup_i8h_grouped_path": (I, [P, I, I, P, P, I, I, I, P, P, P, P, I, P]),
@@ -158,6 +160,20 @@ def moe_route_permute(logits, topk, out=None):
         _ptr(logits), T, E, topk, _ptr(o["topk_ids"]), _ptr(o["topk_w"]), _ptr(o["expert_off"]),
         _ptr(o["sorted_pairs"]), _ptr(o["pair_pos"]), _ptr(o["workspace"]), o["workspace"].numel(),
         _stream(dev)))
+    return o
+
+
+def moe_route_permute_noalloc(logits, topk, out=None):
+    """moe_route_permute without a workspace: the library's own fixed device
+    scratch holds the histograms (1 MiB per GPU; calls that overlap on one
+    GPU race on it). Same results; `out` may hold the five output tensors."""
+    _dev(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    dev = logits.device
+    o = _routing_outputs(out, T, E, topk, dev)
+    _check("moe_route_permute_noalloc", lib().moe_route_permute_noalloc(
+        _ptr(logits), T, E, topk, _ptr(o["topk_ids"]), _ptr(o["topk_w"]), _ptr(o["expert_off"]),
+        _ptr(o["sorted_pairs"]), _ptr(o["pair_pos"]), _stream(dev)))
     return o
 
 

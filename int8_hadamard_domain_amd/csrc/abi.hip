@@ -189,6 +189,25 @@ int moe_route_permute(const float* logits, int T, int E, int topk, int32_t* topk
                                     workspace, as_stream(stream)));
 }
 
+int moe_route_permute_noalloc(const float* logits, int T, int E, int topk, int32_t* topk_ids, float* topk_w,
+                              int32_t* expert_off, int32_t* sorted_pairs, int32_t* pair_pos, void* stream) {
+  // the checks of moe_route_permute, then the scratch size instead of a workspace
+  if (T < 0 || E <= 0 || topk <= 0) return I8H_EINVAL;
+  if (E > kMaxExperts || topk > kMaxTopk || topk > E) return I8H_EUNSUPPORTED;
+  if ((int64_t)T * topk >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;
+  if (((int64_t)T * topk + 255) / 256 * E >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;
+  if (T == 0) return I8H_OK;
+  if (i8h::route_workspace_bytes(T, E, topk) > i8h::kRouteScratchBytes) return I8H_EUNSUPPORTED;
+  if (!logits || !topk_ids || !topk_w || !expert_off || !sorted_pairs || !pair_pos) return I8H_EINVAL;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(expert_off, 4) ||
+      !aligned(sorted_pairs, 4) || !aligned(pair_pos, 4))
+    return I8H_EINVAL;
+  void* ws = nullptr;
+  if (i8h::route_scratch(as_stream(stream), &ws) != hipSuccess) return I8H_EHIP;
+  return from_hip(i8h::launch_route(logits, T, E, topk, topk_ids, topk_w, expert_off, sorted_pairs, pair_pos, ws,
+                                    as_stream(stream)));
+}
+
 int hadamard128_rotate(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy, int T, int K, void* stream) {
   if (T < 0 || K <= 0 || (K % 128) != 0) return I8H_EINVAL;
   if (ldx < K || ldy < K || (ldx % 8) != 0 || (ldy % 8) != 0) return I8H_EINVAL;

@@ -11,6 +11,11 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopk = 32;
 
 size_t route_workspace_bytes(int T, int E, int k);
+// the allocation-free routing call's device scratch: its size, and its
+// address on the current device (which must be the stream's), looked up once
+// per device
+constexpr size_t kRouteScratchBytes = (size_t)1 << 20;
+hipError_t route_scratch(hipStream_t st, void** out);
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                         int32_t* expert_off, int32_t* sorted_pairs, int32_t* pair_pos,
                         void* ws, hipStream_t st);

@@ -15,6 +15,8 @@
 //   k_route_scatter  per chunk: totals + exclusive scan + in-chunk stable ranks
 //   k_route_small    T <= 4: the three steps in one block (decode shape)
 
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "topk.hpp"
@@ -224,6 +226,39 @@ size_t route_workspace_bytes(int T, int E, int k) {
   size_t P = (size_t)T * k;
   size_t nchunks = (P + kChunkPairs - 1) / kChunkPairs;
   return nchunks * (size_t)E * sizeof(int32_t);
+}
+
+// Scratch of the allocation-free routing call: the per-chunk histograms that
+// the caller's workspace holds otherwise. Every GPU the library runs on keeps
+// its own copy until the process ends. k_route_count rewrites every histogram
+// entry a call reads, so nothing needs clearing between calls.
+static __device__ __align__(256) int32_t scratch[kRouteScratchBytes / sizeof(int32_t)];
+
+hipError_t route_scratch(hipStream_t st, void** out) {
+  // the array's name is a host-side stand-in: its device address comes from
+  // hipGetSymbolAddress, once per device with that device current
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (st != nullptr) {
+    int sdev = -1;
+    e = hipStreamGetDevice(st, &sdev);
+    if (e != hipSuccess) return e;
+    if (sdev != dev) return hipErrorInvalidDevice;   // the kernels would run on another GPU's copy
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 #define I8H_TOPK_DISPATCH(KERNEL, ...)                                   \

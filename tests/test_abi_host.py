@@ -33,7 +33,7 @@ def L():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -85,6 +85,22 @@ def test_route_validation(L):
     # P fits in int32, but ceil(P / 256) * E (the chunk histograms' index) does not
     assert route(L, T=1 << 24, k=32, E=1024) == EUNSUP
     assert route(L, T=(1 << 24) - 8, k=32, E=1024, ptr=None) == EINVAL   # just below: other checks apply
+
+
+def test_route_noalloc_validation(L):
+    f = lambda T=8, E=16, k=2, ptr=A: L.moe_route_permute_noalloc(ptr, T, E, k, A, A, A, A, A, None)
+    assert f(T=-1) == EINVAL
+    assert f(E=0) == EINVAL
+    assert f(E=1025) == EUNSUP
+    assert f(E=4, k=5) == EUNSUP
+    assert f(T=0) == OK
+    # the fixed 1 MiB scratch holds ceil(P / 256) * E counts: P = 524288 pairs at E = 128 is the
+    # largest admitted, one chunk more is refused (both before any HIP call)
+    assert L.moe_route_permute_workspace_size(65536, 128, 8) == 1 << 20
+    assert f(T=65536 + 32, E=128, k=8) == EUNSUP
+    assert f(T=65536, E=128, k=8, ptr=None) == EINVAL     # within the limit: the other checks apply
+    assert f(T=1 << 20, E=1024, k=1) == EUNSUP
+    assert f(ptr=ODD) == EINVAL
 
 
 def rot(L, x=A, ldx=256, y=A, ldy=256, T=4, K=256):
