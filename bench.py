@@ -20,7 +20,14 @@ by device synchronisations.
 Printed: one JSON line with the step throughput (weight GB/s: bytes of the
 touched experts' codes and scales per second), tokens/s, the roofline of the
 dominant kernel (gate_up) timed with HIP events over graph replays of that
-kernel alone, and the CPU oracle timed on a bounded sample of the same steps.
+kernel alone, and the CPU oracle timed on a bounded sample of the same steps
+(one thread, then every thread; the CPU model is recorded). The decode step
+is the headline; the verify (T = 128) and prefill (T = 2048) steps are
+measured in the same run and reported under "rows", each with its own
+roofline (HBM, and the bf16 MFMA fraction). Every timed region runs at least
+--steps steps and at least --min-ms of graph replays; the steps actually run
+are reported. A plain HBM read probe (libi8h_probe.so) runs first, and every
+roofline is also given as a fraction of what it reaches on the same GPU.
 """
 
 import argparse
@@ -42,16 +49,27 @@ METRIC = "weight GB/s and tokens/s, MoE gate_up at M=1/128/2048; % HBM / MFMA pe
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--steps", type=int, default=512,
+                    help="least number of timed steps; more are run until the timed region reaches --min-ms")
     ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--min-ms", type=float, default=20.0,
+                    help="least length of each timed region (graph replays), whatever --steps says")
     ap.add_argument("--workload", default="decode", choices=["decode", "verify", "prefill", "fp8", "w8a8"])
+    ap.add_argument("--rows", default="auto",
+                    help="comma list of further workloads measured in the same run and reported under 'rows' "
+                         "(auto: verify,prefill for the decode headline, none otherwise; 'none': skip)")
     ap.add_argument("--copies", type=int, default=0, help="weight copies cycled (0: enough to defeat caches)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="budget of each CPU oracle sample (one thread, then all threads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the live HBM read-bandwidth probe")
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "gemm", "tall", "skinny"])
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 4 times (the reference kernel "
                          "whose FETCH_SIZE / WRITE_SIZE counters scale the HBM traffic figures)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="only run the HBM read-bandwidth probe (streaming and one-shot decode-sized reads) "
+                         "and print its JSON line")
     ap.add_argument("--two-launch", action="store_true",
                     help="decode: time moe_route_permute + moe_gateup_i8h_grouped_fused instead of the "
                          "one-launch moe_route_gateup_i8h_decode")
@@ -67,6 +85,50 @@ def parse():
     return ap.parse_args()
 
 
+def capture_graph(fn, S, dev):
+    """fn(0..S-1) once eagerly on a side stream, then captured into one graph."""
+    import torch
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for i in range(S):
+            fn(i)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(S):
+            fn(i)
+    torch.cuda.synchronize(dev)
+    return g
+
+
+def timed_replays(g, S, args, dev):
+    """Warm up with at least args.warmup steps (whole graphs, at least one),
+    then time at least args.steps steps and at least args.min_ms of replays,
+    bracketed by device synchronisations. Returns (steps, warmup steps, wall
+    seconds, per-step ms from HIP events on the replay stream)."""
+    import torch
+    warm_reps = max(1, -(-args.warmup // S))
+    t0 = time.perf_counter()
+    for _ in range(warm_reps):
+        g.replay()
+    torch.cuda.synchronize(dev)
+    per_rep = (time.perf_counter() - t0) / warm_reps
+    reps = max(1, -(-args.steps // S), int(np.ceil(1.15 * args.min_ms * 1e-3 / max(per_rep, 1e-7))))
+    st = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    ev0.record(st)
+    for _ in range(reps):
+        g.replay()
+    ev1.record(st)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    return reps * S, warm_reps * S, wall, ev0.elapsed_time(ev1) / (reps * S)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -77,7 +139,6 @@ def main():
 
     import torch
     import int8_hadamard_domain_amd as i8h
-    import synth
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -91,16 +152,65 @@ def main():
         torch.cuda.synchronize(dev)
         print(json.dumps({"copy_probe_bytes": args.copy_probe, "copies": 4}))
         return
+    if args.read_probe:
+        print(json.dumps({"read_probe": read_probe(dev)}))
+        return
     i8h.lib()
 
-    name = args.workload
-    L = synth.layer(name)
     if args.stage == "down":
-        bench_down(args, L, dev)
+        bench_down(args, synth_layer(args.workload), dev)
         return
     if args.stage == "linear":
         bench_linear(args, dev)
         return
+
+    probe = None if args.no_probe else read_probe(dev)
+    head = measure_gate_up(args, args.workload, dev, probe, keep_inputs=not args.no_cpu_baseline)
+    if args.rows == "auto":
+        extra = ["verify", "prefill"] if args.workload == "decode" else []
+    elif args.rows in ("", "none"):
+        extra = []
+    else:
+        extra = [w for w in args.rows.split(",") if w]
+    rows = {}
+    for name in extra:
+        torch.cuda.empty_cache()
+        r = measure_gate_up(args, name, dev, probe, keep_inputs=False)
+        r.pop("_cpu", None)
+        rows[name] = r
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(*head.pop("_cpu"), args.cpu_seconds)
+    head.pop("_cpu", None)
+    out = {"metric": METRIC}
+    out.update(head)
+    out["cpu_baseline"] = cpu
+    if rows:
+        out["rows"] = rows
+    if probe is not None:
+        out["read_probe"] = probe
+    print(json.dumps(out))
+
+
+def synth_layer(name):
+    import synth
+    return synth.layer(name)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_I8_PEAK_TOPS = 5000.0
+
+
+def measure_gate_up(args, name, dev, probe, keep_inputs):
+    """One workload of the path: its step captured in HIP graphs and replayed.
+    Returns the bench line's fields for it (value, steps, roofline ...)."""
+    import torch
+    import int8_hadamard_domain_amd as i8h
+    import synth
+
+    L = synth.layer(name)
     fp8 = name == "fp8"
     w8 = name == "w8a8"
     fused = (not fp8) and (not w8) and (not args.unfused) and args.path == "auto" and L.T <= 8
@@ -117,8 +227,6 @@ def main():
     S = nb * copies // np.gcd(nb, copies)          # steps per captured graph: every (batch, copy) pair
     while S > 256:
         S //= 2
-    steps = max(S, (args.steps + S - 1) // S * S)
-    warm = max(S, (args.warmup + S - 1) // S * S)
 
     t_setup = time.perf_counter()
     LB = synth.layer(name, T=L.T * nb)
@@ -151,6 +259,8 @@ def main():
                          dtype=torch.uint8, device=dev)
     i8g_ws = torch.empty((max(i8h.lib().moe_gateup_i8g_workspace_size(L.T, L.K), 1),),
                          dtype=torch.uint8, device=dev)
+    fused_ws = torch.empty((max(i8h.lib().moe_gateup_i8h_fused_workspace_size(L.T, L.K), 1),),
+                           dtype=torch.uint8, device=dev)
 
     def gate_up(i):
         b = route_bufs[i]
@@ -166,7 +276,7 @@ def main():
                                        gate_up=False, act=act, workspace=i8g_ws)
         elif fused:
             i8h.moe_gateup_i8h_grouped_fused(xs[i % nb], codes[c], scales[c], k, b["expert_off"],
-                                             b["sorted_pairs"], gate_up=False, act=act)
+                                             b["sorted_pairs"], gate_up=False, act=act, workspace=fused_ws)
         else:
             i8h.moe_gateup_i8h_grouped(xr, codes[c], scales[c], k, b["expert_off"], b["sorted_pairs"],
                                        gate_up=False, act=act, path=args.path)
@@ -180,22 +290,7 @@ def main():
             i8h.hadamard128_rotate(xs[i % nb], out=xr)
         gate_up(i)
 
-    def capture(fn):
-        side = torch.cuda.Stream(device=dev)
-        side.wait_stream(torch.cuda.current_stream(dev))
-        with torch.cuda.stream(side):
-            for i in range(S):
-                fn(i)
-        torch.cuda.current_stream(dev).wait_stream(side)
-        torch.cuda.synchronize(dev)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(S):
-                fn(i)
-        torch.cuda.synchronize(dev)
-        return g
-
-    g_step = capture(step)
+    g_step = capture_graph(step, S, dev)
     # touched experts of every captured step (bookkeeping only, outside the timed region)
     touched = []
     for i in range(S):
@@ -206,23 +301,14 @@ def main():
     bytes_per_expert = L.N * L.K + (L.N // 128) * L.G * 2 if fp8 else L.N * L.K + L.N * L.G * 2
     weight_bytes = np.array(touched, dtype=np.float64) * bytes_per_expert   # per step in the graph
 
-    for _ in range(warm // S):
-        g_step.replay()
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for _ in range(steps // S):
-        g_step.replay()
-    torch.cuda.synchronize(dev)
-    t1 = time.perf_counter()
-    wall = t1 - t0
+    steps, warm, wall, step_ms_ev = timed_replays(g_step, S, args, dev)
     ms_per_step = wall / steps * 1e3
-    total_weight = weight_bytes.sum() * (steps // S)
-    value = total_weight / wall / 1e9
+    value = weight_bytes.mean() * steps / wall / 1e9
     tokens_per_s = L.T * steps / wall
 
     # ---- dominant kernel: gate_up alone, HIP events around graph replays ----
-    g_gu = capture(gate_up)
-    reps = max(1, 2048 // S)
+    g_gu = capture_graph(gate_up, S, dev)
+    reps = max(2, int(np.ceil(args.min_ms * 1e-3 / max(ms_per_step * 1e-3 * S, 1e-7))))
     for _ in range(2):
         g_gu.replay()
     st = torch.cuda.current_stream(dev)
@@ -234,6 +320,7 @@ def main():
     ev1.record(st)
     torch.cuda.synchronize(dev)
     kern_us = ev0.elapsed_time(ev1) * 1e3 / (reps * S)
+    del g_gu, g_step
     # algorithmic bytes per launch: touched codes + scales, activations read once,
     # act written, routing lists read
     x_bytes = L.T * L.K * (1 if fp8 else 2)
@@ -262,20 +349,25 @@ def main():
         kernel_name, key = "k_gateup_gemm<I8>", "gemm_i8"
     else:
         kernel_name, key = "k_gateup_i8h_skinny (int8, 64-pair passes)", "skinny"
-    traffic = measured_traffic(key, name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": kernel_name,
-                "kernel_us": round(kern_us, 3), "alg_bytes_per_launch": int(alg_bytes),
-                "mfma_tflops": round(flops / (kern_us * 1e-6) / 1e12, 2)}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(key, name),
+                "kernel": kernel_name, "kernel_us": round(kern_us, 3), "alg_bytes_per_launch": int(alg_bytes)}
+    if probe is not None:
+        # against what a plain read reaches on this GPU: a one-shot read of the decode step's size for
+        # the decode kernels, the sustained streaming rate for the others
+        ref = probe["oneshot"]["gbs"] if L.T <= 8 else probe["stream"]["gbs"]
+        roofline["probe_gbs"] = ref
+        roofline["frac_of_probe"] = round(achieved / ref, 4)
+    if w8:
+        tops = flops / (kern_us * 1e-6) / 1e12
+        roofline["mfma"] = {"achieved": round(tops, 1), "peak": MFMA_I8_PEAK_TOPS, "unit": "TOP/s (int8)",
+                            "frac": round(tops / MFMA_I8_PEAK_TOPS, 4)}
+    else:
+        tf = flops / (kern_us * 1e-6) / 1e12
+        roofline["mfma"] = {"achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s (bf16)",
+                            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(L, nb, logits_np, x_np, codes_np, sbits_np, "fp8" if fp8 else "i8g" if w8 else "i8h",
-                           args.cpu_seconds, bytes_per_expert)
-
-    out = {
-        "metric": METRIC,
+    row = {
         "value": round(value, 2),
         "unit": "GB/s",
         "tokens_per_s": round(tokens_per_s, 1),
@@ -283,14 +375,17 @@ def main():
         "steps": int(steps),
         "warmup": int(warm),
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_events": round(step_ms_ev, 5),
+        "timed_region_ms": round(wall * 1e3, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3*fp8e4m3->f32" if fp8 else "i8*i8->i32->f32" if w8 else "i8*bf16->f32",
+        "dtype": "fp8e4m3*bf16(exact)->f32" if fp8 else "i8*i8->i32->f32" if w8 else "i8*bf16->f32",
         "data": "synthetic",
         "config": {"workload": f"{name}: T={L.T} K={L.K} E={L.E} top-{k} N={L.N} (gate_up of Gemma 4 26B-A4B)",
                    "T": L.T, "K": L.K, "E": L.E, "topk": k, "N": L.N, "weight_copies": int(copies),
                    "steps_per_graph": int(S), "touched_experts_per_step": float(np.mean(touched)),
+                   "steps_requested": int(args.steps), "warmup_requested": int(args.warmup),
                    "outputs": "act (fp32); gate_up not stored", "setup_s": round(setup_s, 1),
                    "step": ("route -> rotate -> gate_up in one launch" if one_launch else
                             "route -> gate_up (FP8 quantizer + product)" if fp8 else
@@ -298,9 +393,79 @@ def main():
                             "route -> gate_up with the rotation fused" if fused else
                             "route -> rotate -> gate_up")},
         "roofline": roofline,
-        "cpu_baseline": cpu,
     }
-    print(json.dumps(out))
+    if keep_inputs:
+        row["_cpu"] = (L, nb, logits_np, x_np, codes_np, sbits_np, "fp8" if fp8 else "i8g" if w8 else "i8h",
+                       bytes_per_expert)
+    del codes, scales, codes0, scales0
+    return row
+
+
+def read_probe(dev):
+    """HBM read bandwidth on this GPU with the plainest read kernel
+    (libi8h_probe.so): a sustained stream over 2 GiB, and one-shot reads of
+    the decode step's touched bytes (8 experts' codes and scales, 25.56 MB),
+    16 buffers cycled in a graph of 64 launches so no read finds its buffer in
+    the 256 MB last-level cache. Several grid sizes; the best of each."""
+    import ctypes
+    import torch
+    here = os.path.dirname(os.path.abspath(__file__))
+    P = ctypes.CDLL(os.path.join(here, "int8_hadamard_domain_amd", "lib", "libi8h_probe.so"))
+    P.i8h_read_probe.restype = ctypes.c_int
+    P.i8h_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint32,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    key = 0x9E3779B9
+    max_blocks = 65536
+    sink = torch.zeros(max_blocks * 256, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream(dev)
+
+    def launch(buf, nbytes, blocks):
+        # on the stream current at the call (the capturing one inside a graph capture)
+        cur = torch.cuda.current_stream(dev).cuda_stream
+        rc = P.i8h_read_probe(ctypes.c_void_p(buf.data_ptr()), nbytes, blocks, key, ctypes.c_void_p(sink.data_ptr()),
+                              ctypes.c_void_p(cur))
+        if rc != 0:
+            raise RuntimeError(f"i8h_read_probe failed ({rc})")
+
+    def time_graph(fn, n_launch, reps):
+        g = capture_graph(fn, n_launch, dev)
+        for _ in range(2):
+            g.replay()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        ev0.record(st)
+        for _ in range(reps):
+            g.replay()
+        ev1.record(st)
+        torch.cuda.synchronize(dev)
+        return ev0.elapsed_time(ev1) * 1e-3 / (reps * n_launch)
+
+    out = {}
+    big = 2 << 30
+    buf = torch.ones(big // 4, dtype=torch.int32, device=dev)
+    best = None
+    for per_thread in (8, 32, 128):
+        blocks = min(max_blocks, -(-big // (16 * 256 * per_thread)))
+        t = time_graph(lambda i: launch(buf, big, blocks), 4, 3)
+        if best is None or t < best[0]:
+            best = (t, blocks)
+    out["stream"] = {"bytes": big, "us": round(best[0] * 1e6, 2), "gbs": round(big / best[0] / 1e9, 1),
+                     "blocks": best[1], "frac_of_peak": round(big / best[0] / 1e9 / HBM_PEAK_GBS, 4)}
+    del buf
+    one = 8 * (1536 * 2048 + 1536 * 16 * 2)        # the decode step's touched weight bytes
+    bufs = [torch.ones(one // 4, dtype=torch.int32, device=dev) for _ in range(16)]
+    best = None
+    for per_thread in (8, 16, 32):
+        blocks = -(-one // (16 * 256 * per_thread))
+        t = time_graph(lambda i: launch(bufs[i % 16], one, blocks), 64, 8)
+        if best is None or t < best[0]:
+            best = (t, blocks)
+    out["oneshot"] = {"bytes": one, "us": round(best[0] * 1e6, 3), "gbs": round(one / best[0] / 1e9, 1),
+                      "blocks": best[1], "frac_of_peak": round(one / best[0] / 1e9 / HBM_PEAK_GBS, 4),
+                      "note": "per launch inside a graph of 64, 16 buffers cycled"}
+    del bufs, sink
+    torch.cuda.empty_cache()
+    return out
 
 
 # device-code sources of each timed kernel: a traffic figure holds only for the sources it was
@@ -358,8 +523,6 @@ def bench_down(args, L, dev):
     S = nb * copies // np.gcd(nb, copies)
     while S > 256:
         S //= 2
-    steps = max(S, (args.steps + S - 1) // S * S)
-    warm = max(S, (args.warmup + S - 1) // S * S)
 
     t_setup = time.perf_counter()
     LB = synth.layer(L.name, T=L.T * nb)
@@ -378,36 +541,14 @@ def bench_down(args, L, dev):
     def step(i):
         i8h.moe_down_bf16_combine(acts[i % nb], ws_[i % copies], routes[i % nb], out=out, workspace=work)
 
-    side = torch.cuda.Stream(device=dev)
-    side.wait_stream(torch.cuda.current_stream(dev))
-    with torch.cuda.stream(side):
-        for i in range(S):
-            step(i)
-    torch.cuda.current_stream(dev).wait_stream(side)
-    torch.cuda.synchronize(dev)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(S):
-            step(i)
-    torch.cuda.synchronize(dev)
+    g = capture_graph(step, S, dev)
     touched = [int(np.count_nonzero(np.diff(routes[i % nb]["expert_off"].cpu().numpy()))) for i in range(S)]
     setup_s = time.perf_counter() - t_setup
     wbytes = np.array(touched, dtype=np.float64) * H * I * 2
 
-    for _ in range(warm // S):
-        g.replay()
-    torch.cuda.synchronize(dev)
-    st = torch.cuda.current_stream(dev)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(st)
-    for _ in range(steps // S):
-        g.replay()
-    ev1.record(st)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    call_us = ev0.elapsed_time(ev1) * 1e3 / steps
-    value = wbytes.sum() * (steps // S) / wall / 1e9
+    steps, warm, wall, step_ms_ev = timed_replays(g, S, args, dev)
+    call_us = step_ms_ev * 1e3
+    value = wbytes.mean() * steps / wall / 1e9
     # algorithmic bytes per call: touched W_down, act read once, out written, routing lists
     alg = wbytes.mean() + L.P * I * 4 + L.T * H * 4 + L.P * 4 * 3 + (L.E + 1) * 4
     achieved = alg / (call_us * 1e-6) / 1e9
@@ -480,8 +621,6 @@ def bench_linear(args, dev):
     wbytes = N * K + N * (K // 128) * 2
     copies = args.copies if args.copies > 0 else int(min(256, max(2, np.ceil(1.6e9 / wbytes))))
     S = copies
-    steps = max(S, (args.steps + S - 1) // S * S)
-    warm = max(S, (args.warmup + S - 1) // S * S)
     t_setup = time.perf_counter()
     q_np, s_np = synth.synthetic_i8f16(N, K, d["seed"])
     x_np = synth.drafter_activations_bf16(T, K, d["seed"])
@@ -495,32 +634,10 @@ def bench_linear(args, dev):
     def step(i):
         i8h.linear_i8f16(x, qs[i % copies], ss[i % copies], out=y)
 
-    side = torch.cuda.Stream(device=dev)
-    side.wait_stream(torch.cuda.current_stream(dev))
-    with torch.cuda.stream(side):
-        for i in range(S):
-            step(i)
-    torch.cuda.current_stream(dev).wait_stream(side)
-    torch.cuda.synchronize(dev)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(S):
-            step(i)
-    torch.cuda.synchronize(dev)
+    g = capture_graph(step, S, dev)
     setup_s = time.perf_counter() - t_setup
-    for _ in range(warm // S):
-        g.replay()
-    torch.cuda.synchronize(dev)
-    st = torch.cuda.current_stream(dev)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(st)
-    for _ in range(steps // S):
-        g.replay()
-    ev1.record(st)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    call_us = ev0.elapsed_time(ev1) * 1e3 / steps
+    steps, warm, wall, step_ms_ev = timed_replays(g, S, args, dev)
+    call_us = step_ms_ev * 1e3
     alg = wbytes + T * K * 2 + T * N * 4
     achieved = alg / (call_us * 1e-6) / 1e9
     cpu = None
@@ -566,41 +683,76 @@ def bench_linear(args, dev):
     }))
 
 
-def cpu_baseline(L, nb, logits_np, x_np, codes_np, sbits_np, fmt, budget_s, bytes_per_expert):
-    """The fp64 oracle, as it stands, on the same steps until the budget is spent."""
-    from oracle import gateup, hadamard, numfmt, quant, router, w8a8
+def host_cpu():
+    """CPU model and the threads this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return model, avail
+
+
+def blas_threads():
     try:
         import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        cores = max([d.get("num_threads", 1) for d in info] + [1])
+        return max([d.get("num_threads", 1) for d in threadpoolctl.threadpool_info()] + [1])
     except Exception:
-        cores = 1
+        return 1
+
+
+def cpu_baseline(L, nb, logits_np, x_np, codes_np, sbits_np, fmt, bytes_per_expert, budget_s):
+    """The fp64 oracle, as it stands, on the same steps until the budget is
+    spent: once restricted to one thread, once with every thread its BLAS
+    uses on this host."""
+    import threadpoolctl
+    from oracle import gateup, hadamard, numfmt, quant, router, w8a8
+
     scales = numfmt.bf16_from_bits(sbits_np)
-    done, wbytes, tokens = 0, 0.0, 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s or done == 0:      # cycles through the step batches
-        lg = logits_np[done % nb]
-        x = numfmt.bf16_from_bits(x_np[done % nb])
-        r = router.route(lg, L.topk)
-        if fmt == "fp8":
-            qx, sx = quant.quantize_fp8_activations(x)
-            gu = gateup.gateup_fp8blk(qx, sx, codes_np, scales, r["expert_off"], r["sorted_pairs"], L.topk)
-        elif fmt == "i8g":
-            qx, sx = w8a8.quantize_i8_activations(x)
-            gu = w8a8.gateup_i8g(qx, sx, codes_np, scales, r["expert_off"], r["sorted_pairs"], L.topk)
-        else:
-            xr = hadamard.rotate_activations_bf16(x)
-            gu = gateup.gateup_i8h(xr, codes_np, scales, r["expert_off"], r["sorted_pairs"], L.topk)
-        gateup.epilogue(gu)
-        done += 1
-        wbytes += np.count_nonzero(np.diff(r["expert_off"])) * bytes_per_expert
-        tokens += L.T
-    el = time.perf_counter() - t0
-    return {"value": round(wbytes / el / 1e9, 4), "unit": "GB/s", "tokens_per_s": round(tokens / el, 3),
-            "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} step(s) of the same workload (route + "
-                      f"{'rotate' if fmt == 'i8h' else 'quantize'} + gate_up + epilogue, fp64 NumPy), "
-                      f"{el:.1f} s"}
+
+    def run(budget):
+        done, wbytes, tokens = 0, 0.0, 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget or done == 0:      # cycles through the step batches
+            lg = logits_np[done % nb]
+            x = numfmt.bf16_from_bits(x_np[done % nb])
+            r = router.route(lg, L.topk)
+            if fmt == "fp8":
+                qx, sx = quant.quantize_fp8_activations(x)
+                gu = gateup.gateup_fp8blk(qx, sx, codes_np, scales, r["expert_off"], r["sorted_pairs"], L.topk)
+            elif fmt == "i8g":
+                qx, sx = w8a8.quantize_i8_activations(x)
+                gu = w8a8.gateup_i8g(qx, sx, codes_np, scales, r["expert_off"], r["sorted_pairs"], L.topk)
+            else:
+                xr = hadamard.rotate_activations_bf16(x)
+                gu = gateup.gateup_i8h(xr, codes_np, scales, r["expert_off"], r["sorted_pairs"], L.topk)
+            gateup.epilogue(gu)
+            done += 1
+            wbytes += np.count_nonzero(np.diff(r["expert_off"])) * bytes_per_expert
+            tokens += L.T
+        el = time.perf_counter() - t0
+        return done, wbytes / el / 1e9, tokens / el, el
+
+    model, avail = host_cpu()
+    with threadpoolctl.threadpool_limits(limits=1):
+        d1, v1, t1, e1 = run(budget_s)
+    threads = blas_threads()
+    dn, vn, tn, en = run(budget_s)
+    what = f"route + {'rotate' if fmt == 'i8h' else 'quantize'} + gate_up + epilogue, fp64 NumPy"
+    return {"value": round(vn, 4), "unit": "GB/s", "tokens_per_s": round(tn, 3), "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{dn} step(s) of the same workload ({what}), {en:.1f} s, {threads} BLAS threads",
+            "single_thread": {"value": round(v1, 4), "unit": "GB/s", "tokens_per_s": round(t1, 3), "cores": 1,
+                              "sample": f"{d1} step(s), {e1:.1f} s"},
+            "cpu_model": model, "cpus_available": int(avail)}
 
 
 if __name__ == "__main__":
