@@ -398,6 +398,88 @@ __device__ __forceinline__ void read_rotated(const uint16_t* s_xr, float (&xv)[N
   }
 }
 
+// One token: the k chosen experts hold one pair each, so the sorted row of a
+// workgroup's slot s is s and its expert is the s-th chosen one in index
+// order. Every wave finds the chosen set itself (topk_mask: registers and
+// ballots only), picks its expert and issues its code loads, with no LDS
+// round trip and no barrier before them. Workgroup (0, 0) then ranks the
+// chosen experts (slot order, softmax weights) and stores the routing
+// outputs while its codes arrive.
+template <int NCH, int RPW, int VPL>
+__device__ __forceinline__ void decode_one_token(const float* __restrict__ logits, const uint16_t* __restrict__ x,
+                                                 int K, const int8_t* __restrict__ codes,
+                                                 const uint16_t* __restrict__ scales, int E, int N, int k,
+                                                 int32_t* __restrict__ ids_out, float* __restrict__ w_out,
+                                                 int32_t* __restrict__ expert_off,
+                                                 int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos,
+                                                 float* __restrict__ gu, float* __restrict__ act,
+                                                 uint64_t* s_rank, uint16_t* s_xr, int wave, int lane) {
+  const int I = N / 2;
+  const bool writer = blockIdx.x == 0 && blockIdx.y == 0;
+  float lv[VPL];
+  load_logits<VPL>(logits, E, lane, lv);
+  RotShare<NCH> share;
+  share.load(x, K, wave, lane);                 // needed whatever the routing
+  uint64_t chosen[VPL];
+  topk_mask<VPL>(lv, E, k, lane, chosen);
+  // the expert of this block's slot: the blockIdx.y-th chosen one in index order
+  int e = -1, rem = blockIdx.y;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int c = __popcll(chosen[i]);
+    if (e < 0) {
+      if (rem < c) {
+        uint64_t m = chosen[i];
+        for (int q = 0; q < rem; ++q) m &= m - 1;
+        e = kWave * i + __ffsll((unsigned long long)m) - 1;
+      } else {
+        rem -= c;
+      }
+    }
+  }
+  // routing outputs from the chosen set (ranks and weights from the ranked
+  // top-k of the same rule): ids and weights in slot order, the sorted row of
+  // pair j = the number of chosen experts below its expert, expert_off
+  auto store_routing = [&]() {
+    if (wave != 0) return;
+    int id;
+    float wt;
+    wave_topk_fast<VPL>(lv, E, k, lane, id, wt, s_rank);
+    auto chosen_below = [&](int ex) {
+      int c = 0;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int lo = ex - kWave * i;           // chosen entries of word i with index < ex
+        c += lo <= 0 ? 0 : lo >= kWave ? __popcll(chosen[i]) : __popcll(chosen[i] & ((1ull << lo) - 1));
+      }
+      return c;
+    };
+    if (lane < k) {
+      const int row = chosen_below(id);
+      ids_out[lane] = id;
+      w_out[lane] = wt;
+      sorted_pairs[row] = lane;
+      pair_pos[lane] = row;
+    }
+    for (int ex = lane; ex <= E; ex += kWave) expert_off[ex] = chosen_below(ex);
+  };
+  const int i0 = (blockIdx.x * kDecWaves + wave) * RPW;
+  if (e < 0 || i0 >= I) {                       // the same for every wave of the block
+    if (writer) store_routing();
+    return;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  WaveRows<NCH, RPW> R;
+  load_rows(R, codes, scales, e, N, K, i0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  if (writer) store_routing();
+  share.rotate_to(s_xr, wave, lane);            // runs while the codes arrive
+  __syncthreads();
+  float xv[NCH][16];
+  read_rotated<NCH>(s_xr, xv, lane);
+  gemv_row<NCH, RPW, true>(R, xv, K, N, i0, (size_t)blockIdx.y, gu, act, lane);
+}
+
 template <int NCH, int RPW, int VPL>
 __global__ void __launch_bounds__(kDecThreads)
 k_route_gateup_decode(const float* __restrict__ logits, const uint16_t* __restrict__ x, int T, int K,
@@ -414,6 +496,11 @@ k_route_gateup_decode(const float* __restrict__ logits, const uint16_t* __restri
   const int I = N / 2;
   const bool writer = blockIdx.x == 0 && blockIdx.y == 0;  // stores the routing outputs
   const int P = T * k;                                     // <= 64
+  if (T == 1) {
+    decode_one_token<NCH, RPW, VPL>(logits, x, K, codes, scales, E, N, k, ids_out, w_out, expert_off, sorted_pairs,
+                                    pair_pos, gu, act, s_rank[0], s_xr, wave, lane);
+    return;
+  }
 
   // the first token's logits go out first; with a single token its
   // activations are needed whatever the routing, so they follow at once and

@@ -167,6 +167,53 @@ __device__ __forceinline__ void wave_topk_fast(const float (&v)[VPL], int E, int
   weight = lane < k ? ex / sum : 0.0f;
 }
 
+// The set of the k largest entries of one token (the same rule: larger
+// order key first, ties to the lower index, NaN last), as one bit per lane
+// for each of a lane's VPL entries, with no LDS: bisection over the 32 bits
+// of the order keys for the largest threshold with at least k keys at or
+// above it (each step one ballot count per entry), then every key above the
+// threshold and, of the keys equal to it, the lowest indices. The search
+// stops early once exactly k keys lie at or above a candidate: those are the
+// k largest, ties impossible. Wave-uniform result; k <= E.
+template <int VPL>
+__device__ __forceinline__ void topk_mask(const float (&v)[VPL], int E, int k, int lane, uint64_t (&chosen)[VPL]) {
+  // entries past E take key 0 like NaN: no candidate (never 0) counts them,
+  // and only a threshold of 0 needs the index bound (ties below)
+  uint32_t kv[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) kv[i] = lane + kWave * i < E ? order_key(v[i]) : 0u;
+  uint32_t thr = 0;
+  bool exact = false;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = thr | (1u << b);
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) c += __popcll(__ballot(kv[i] >= cand));
+    if (c >= k) {
+      thr = cand;
+      if (c == k) {
+        exact = true;
+        break;
+      }
+    }
+  }
+  int need = k;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    chosen[i] = __ballot(exact ? kv[i] >= thr : kv[i] > thr);   // thr > 0 when exact
+    need -= __popcll(chosen[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    uint64_t eq = __ballot(kv[i] == thr && lane + kWave * i < E);
+    while (need > 0 && eq != 0) {       // ties at the threshold: lowest indices first
+      chosen[i] |= eq & (~eq + 1);
+      eq &= eq - 1;
+      --need;
+    }
+  }
+}
+
 // Grouping of up to 64 pairs by expert inside one wave: lane p holds pair p
 // (valid) routed to expert e (0 <= e < 2^nbits). Radix over the bits of e,
 // most significant first, with one ballot per bit:
