@@ -4,8 +4,9 @@
 One step = one pass of the whole path over one batch of tokens of a routed-
 expert gate_up layer (Gemma 4 26B-A4B shapes: hidden 2048, 128 experts,
 top-8, 2 x 768 gate_up rows per expert):
-    moe_route_permute -> hadamard128_rotate -> moe_gateup_i8h_grouped (act out)
-For a few tokens the three run as one launch (moe_route_gateup_i8h_decode);
+    moe_route_permute_rotate -> moe_gateup_i8h_grouped (act out)
+(the routing kernel rotates the activation rows of the tokens it routes).
+For a few tokens everything runs as one launch (moe_route_gateup_i8h_decode);
 for the FP8 block variant the step is moe_route_permute -> moe_gateup_fp8blk_grouped,
 for the W8A8 int8 g128 form (workload w8a8, prefill sizes) moe_route_permute ->
 moe_gateup_i8g_grouped.
@@ -74,8 +75,9 @@ def parse():
                     help="decode: time moe_route_permute + moe_gateup_i8h_grouped_fused instead of the "
                          "one-launch moe_route_gateup_i8h_decode")
     ap.add_argument("--unfused", action="store_true",
-                    help="rotate with hadamard128_rotate, then moe_gateup_i8h_grouped (default for decode: "
-                         "moe_gateup_i8h_grouped_fused, rotation inside the gate_up kernel)")
+                    help="rotate with hadamard128_rotate as a call of its own, then moe_gateup_i8h_grouped "
+                         "(defaults: decode rotates inside the gate_up kernel, many tokens inside the routing "
+                         "kernel, moe_route_permute_rotate)")
     ap.add_argument("--stage", default="gate_up", choices=["gate_up", "down", "linear"],
                     help="down: time the step after the path instead, moe_down_bf16_combine (bf16 grouped down "
                          "projection + weighted combine) on the workload's token count, with the routing "
@@ -285,9 +287,14 @@ def measure_gate_up(args, name, dev, probe, keep_inputs):
         if one_launch:           # routing is inside the kernel
             gate_up(i)
             return
-        i8h.moe_route_permute(logits[i % nb], k, out=route_bufs[i])
         if not fp8 and not w8 and not fused:
-            i8h.hadamard128_rotate(xs[i % nb], out=xr)
+            if args.unfused:     # the rotation as a call of its own
+                i8h.moe_route_permute(logits[i % nb], k, out=route_bufs[i])
+                i8h.hadamard128_rotate(xs[i % nb], out=xr)
+            else:                # the routing kernel rotates the rows it routes
+                i8h.moe_route_permute_rotate(logits[i % nb], xs[i % nb], k, out=route_bufs[i], x_rot=xr)
+        else:
+            i8h.moe_route_permute(logits[i % nb], k, out=route_bufs[i])
         gate_up(i)
 
     g_step = capture_graph(step, S, dev)
@@ -391,7 +398,8 @@ def measure_gate_up(args, name, dev, probe, keep_inputs):
                             "route -> gate_up (FP8 quantizer + product)" if fp8 else
                             "route -> gate_up (int8 activation quantizer + int8 product)" if w8 else
                             "route -> gate_up with the rotation fused" if fused else
-                            "route -> rotate -> gate_up")},
+                            "route -> rotate -> gate_up" if args.unfused else
+                            "route + rotate (one kernel) -> gate_up")},
         "roofline": roofline,
     }
     if keep_inputs:

@@ -84,9 +84,11 @@ const char* i8h_status_string(int status);
  * sorted_pairs[P] int32 out
  * pair_pos    [P] int32 out
  * workspace   device scratch of at least moe_route_permute_workspace_size()
- *             bytes (may be NULL when that size is 0); contents on entry
- *             are ignored. P must stay below 2^31, and ceil(P / 256) * E
- *             too (else I8H_EUNSUPPORTED).
+ *             bytes (may be NULL when that size is 0): one histogram of E
+ *             int32 counts per chunk of c = max(1, min(floor(256 / topk),
+ *             ceil(T / 32))) whole tokens, C = ceil(T / c) chunks (none for
+ *             T <= 4); contents on entry are ignored. P must stay below
+ *             2^31, and C * E too (else I8H_EUNSUPPORTED).
  * ---------------------------------------------------------------------- */
 size_t moe_route_permute_workspace_size(int T, int E, int topk);
 int moe_route_permute(const float* logits, int T, int E, int topk,
@@ -94,14 +96,29 @@ int moe_route_permute(const float* logits, int T, int E, int topk,
                       int32_t* sorted_pairs, int32_t* pair_pos,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_route_permute that also rotates the activation rows of the tokens it
+ * routes: the int8 card's model table (row "Needs") puts the 128-wide
+ * Hadamard rotation in the producer of the experts' input, and the routing
+ * is that producer here. Same routing outputs, rules and workspace as
+ * moe_route_permute, bit for bit; x_rot equals hadamard128_rotate(x) bit for
+ * bit. x [T, K] bf16 (K % 128 == 0, rows contiguous, 16-B aligned), x_rot
+ * [T, K] bf16 out (16-B aligned); x == x_rot (in place) is allowed, other
+ * overlap is not; T*K < 2^31 (else I8H_EUNSUPPORTED). For many tokens the
+ * rotation runs inside the routing kernel (one launch fewer than the two
+ * calls); for T <= 4 it is a launch of its own after the routing. */
+int moe_route_permute_rotate(const float* logits, const uint16_t* x, int T, int E, int topk, int K,
+                             int32_t* topk_ids, float* topk_w, int32_t* expert_off,
+                             int32_t* sorted_pairs, int32_t* pair_pos, uint16_t* x_rot,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* moe_route_permute without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc). Same inputs, outputs, rules and results,
  * bit for bit. The call allocates nothing: the histograms that the workspace
  * holds otherwise live in a fixed 1 MiB device array inside the library, one
- * per GPU, held until the process ends; so ceil(T*topk / 256) * E * 4 bytes
- * (moe_route_permute_workspace_size) must not exceed 1 MiB (else
- * I8H_EUNSUPPORTED; e.g. T*topk <= 524,288 pairs at E = 128). The array's
+ * per GPU, held until the process ends; so moe_route_permute_workspace_size
+ * (T, E, topk) must not exceed 1 MiB (else I8H_EUNSUPPORTED; e.g. T*topk <=
+ * 524,288 pairs at E = 128, topk = 8). The array's
  * device address is looked up on the first call on each device: the stream
  * must belong to the current device (else I8H_EHIP). Every call on one GPU
  * shares that array: calls that overlap on one GPU (on different streams, or

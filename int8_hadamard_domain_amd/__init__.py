@@ -9,6 +9,7 @@ the library is not built, or a tensor is not on the GPU, the call raises.
 Functions (same names as the C entry points):
   moe_route_permute          top-k routing and the expert-sorted permutation
   moe_route_permute_noalloc  the same without a workspace (fixed device scratch)
+  moe_route_permute_rotate   routing plus the rotation of the routed tokens' rows
   hadamard128_rotate         blockwise 128-wide Walsh-Hadamard rotation (bf16)
   moe_gateup_i8h_grouped     grouped int8 Hadamard-domain gate_up + GELU epilogue
   moe_gateup_i8h_grouped_fused  the same on unrotated activations (rotation fused)
@@ -60,6 +61,7 @@ def lib():
         "moe_route_permute_workspace_size": (SZ, [I, I, I]),
         "moe_route_permute": (I, [P, I, I, I, P, P, P, P, P, P, SZ, P]),
         "moe_route_permute_noalloc": (I, [P, I, I, I, P, P, P, P, P, P]),
+        "moe_route_permute_rotate": (I, [P, P, I, I, I, I, P, P, P, P, P, P, P, SZ, P]),
         "hadamard128_rotate": (I, [P, I64, P, I64, I, I, P]),
         "moe_gateup_i8h_grouped": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P]),
         "moe_gateup_i8h_grouped_path": (I, [P, I, I, P, P, I, I, I, P, P, P, P, I, P]),
@@ -160,6 +162,28 @@ def moe_route_permute(logits, topk, out=None):
         _ptr(logits), T, E, topk, _ptr(o["topk_ids"]), _ptr(o["topk_w"]), _ptr(o["expert_off"]),
         _ptr(o["sorted_pairs"]), _ptr(o["pair_pos"]), _ptr(o["workspace"]), o["workspace"].numel(),
         _stream(dev)))
+    return o
+
+
+def moe_route_permute_rotate(logits, x, topk, out=None, x_rot=None):
+    """moe_route_permute on logits [T, E] float32, and the 128-wide Hadamard
+    rotation of the activation rows x [T, K] bf16 in the same pass: returns
+    the routing dict with "x_rot" [T, K] bf16 added (x_rot may be x itself)."""
+    _dev(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    dev = logits.device
+    _dev(x, "x", torch.bfloat16, 2, device=dev)
+    K = x.shape[1]
+    _dev(x, "x", torch.bfloat16, shape=(T, K))
+    o = _routing_outputs(out, T, E, topk, dev)
+    xr = torch.empty_like(x) if x_rot is None else _dev(x_rot, "x_rot", torch.bfloat16, shape=(T, K), device=dev)
+    ws_bytes = lib().moe_route_permute_workspace_size(T, E, topk)
+    o["workspace"] = _workspace(o.get("workspace"), "workspace", ws_bytes, dev)
+    _check("moe_route_permute_rotate", lib().moe_route_permute_rotate(
+        _ptr(logits), _ptr(x), T, E, topk, K, _ptr(o["topk_ids"]), _ptr(o["topk_w"]), _ptr(o["expert_off"]),
+        _ptr(o["sorted_pairs"]), _ptr(o["pair_pos"]), _ptr(xr), _ptr(o["workspace"]), o["workspace"].numel(),
+        _stream(dev)))
+    o["x_rot"] = xr
     return o
 
 

@@ -176,8 +176,8 @@ int moe_route_permute(const float* logits, int T, int E, int topk, int32_t* topk
   if (T < 0 || E <= 0 || topk <= 0) return I8H_EINVAL;
   if (E > kMaxExperts || topk > kMaxTopk || topk > E) return I8H_EUNSUPPORTED;
   if ((int64_t)T * topk >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;
-  // the chunk histograms (256 pairs a chunk, E counts each) are indexed in 32 bits
-  if (((int64_t)T * topk + 255) / 256 * E >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;
+  // the chunk histograms (E counts per chunk of whole tokens) are indexed in 32 bits
+  if (i8h::route_chunks(T, topk) * E >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;
   if (T == 0) return I8H_OK;
   if (!logits || !topk_ids || !topk_w || !expert_off || !sorted_pairs || !pair_pos) return I8H_EINVAL;
   if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(expert_off, 4) ||
@@ -186,7 +186,34 @@ int moe_route_permute(const float* logits, int T, int E, int topk, int32_t* topk
   size_t need = i8h::route_workspace_bytes(T, E, topk);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 4))) return I8H_EINVAL;
   return from_hip(i8h::launch_route(logits, T, E, topk, topk_ids, topk_w, expert_off, sorted_pairs, pair_pos,
-                                    workspace, as_stream(stream)));
+                                    workspace, nullptr, nullptr, 0, as_stream(stream)));
+}
+
+int moe_route_permute_rotate(const float* logits, const uint16_t* x, int T, int E, int topk, int K,
+                             int32_t* topk_ids, float* topk_w, int32_t* expert_off, int32_t* sorted_pairs,
+                             int32_t* pair_pos, uint16_t* x_rot, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (T < 0 || E <= 0 || topk <= 0 || K <= 0 || (K % 128) != 0) return I8H_EINVAL;
+  if (E > kMaxExperts || topk > kMaxTopk || topk > E) return I8H_EUNSUPPORTED;
+  if ((int64_t)T * topk >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;
+  if ((int64_t)T * K >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;     // activation offsets
+  if (i8h::route_chunks(T, topk) * E >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;
+  if (T == 0) return I8H_OK;
+  if (!logits || !x || !x_rot || !topk_ids || !topk_w || !expert_off || !sorted_pairs || !pair_pos)
+    return I8H_EINVAL;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(expert_off, 4) ||
+      !aligned(sorted_pairs, 4) || !aligned(pair_pos, 4) || !aligned(x, 16) || !aligned(x_rot, 16))
+    return I8H_EINVAL;
+  if (x != x_rot) {
+    // other overlap would let one row's rotation read what another already wrote
+    uintptr_t xb = reinterpret_cast<uintptr_t>(x), yb = reinterpret_cast<uintptr_t>(x_rot);
+    uintptr_t bytes = 2 * (uintptr_t)((int64_t)T * K);
+    if (xb < yb + bytes && yb < xb + bytes) return I8H_EINVAL;
+  }
+  size_t need = i8h::route_workspace_bytes(T, E, topk);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 4))) return I8H_EINVAL;
+  return from_hip(i8h::launch_route(logits, T, E, topk, topk_ids, topk_w, expert_off, sorted_pairs, pair_pos,
+                                    workspace, x, x_rot, K, as_stream(stream)));
 }
 
 int moe_route_permute_noalloc(const float* logits, int T, int E, int topk, int32_t* topk_ids, float* topk_w,
@@ -195,7 +222,7 @@ int moe_route_permute_noalloc(const float* logits, int T, int E, int topk, int32
   if (T < 0 || E <= 0 || topk <= 0) return I8H_EINVAL;
   if (E > kMaxExperts || topk > kMaxTopk || topk > E) return I8H_EUNSUPPORTED;
   if ((int64_t)T * topk >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;
-  if (((int64_t)T * topk + 255) / 256 * E >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;
+  if (i8h::route_chunks(T, topk) * E >= (int64_t)1 << 31) return I8H_EUNSUPPORTED;
   if (T == 0) return I8H_OK;
   if (i8h::route_workspace_bytes(T, E, topk) > i8h::kRouteScratchBytes) return I8H_EUNSUPPORTED;
   if (!logits || !topk_ids || !topk_w || !expert_off || !sorted_pairs || !pair_pos) return I8H_EINVAL;
@@ -205,7 +232,7 @@ int moe_route_permute_noalloc(const float* logits, int T, int E, int topk, int32
   void* ws = nullptr;
   if (i8h::route_scratch(as_stream(stream), &ws) != hipSuccess) return I8H_EHIP;
   return from_hip(i8h::launch_route(logits, T, E, topk, topk_ids, topk_w, expert_off, sorted_pairs, pair_pos, ws,
-                                    as_stream(stream)));
+                                    nullptr, nullptr, 0, as_stream(stream)));
 }
 
 int hadamard128_rotate(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy, int T, int K, void* stream) {

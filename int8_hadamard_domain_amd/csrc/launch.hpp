@@ -10,15 +10,18 @@ namespace i8h {
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopk = 32;
 
+// chunks of whole tokens (at most 256 pairs each) of the many-token routing
+int64_t route_chunks(int T, int k);
 size_t route_workspace_bytes(int T, int E, int k);
 // the allocation-free routing call's device scratch: its size, and its
 // address on the current device (which must be the stream's), looked up once
 // per device
 constexpr size_t kRouteScratchBytes = (size_t)1 << 20;
 hipError_t route_scratch(hipStream_t st, void** out);
+// x != NULL also rotates the T activation rows x [T, K] into xr (x may be xr)
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                         int32_t* expert_off, int32_t* sorted_pairs, int32_t* pair_pos,
-                        void* ws, hipStream_t st);
+                        void* ws, const uint16_t* x, uint16_t* xr, int K, hipStream_t st);
 
 hipError_t launch_fwht128(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy, int T, int K,
                           hipStream_t st);

@@ -10,8 +10,11 @@
 // ballots in lane order and fixed block order, never from atomic arrival order.
 //
 // Kernels
-//   k_route_topk     one wave per token (grid T/4 x 256 threads)
-//   k_route_count    per chunk of 256 pairs: histogram over experts (LDS)
+//   k_route_rows     per chunk of tokens (at most 256 pairs): top-k of every
+//                    token (a wave per token) and the chunk's histogram over
+//                    experts (LDS); optionally, in further workgroups of the
+//                    same launch, the 128-wide Hadamard rotation of the token
+//                    rows (the routing is the producer of the experts' input)
 //   k_route_scatter  per chunk: totals + exclusive scan + in-chunk stable ranks
 //   k_route_small    T <= 4: the three steps in one block (decode shape)
 
@@ -19,39 +22,76 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "rotate.hpp"
 #include "topk.hpp"
 
 namespace i8h {
 
-constexpr int kChunkPairs = 256;   // pairs per histogram/scatter block
+constexpr int kChunkPairs = 256;   // most pairs per histogram/scatter chunk
 constexpr int kRouteThreads = 256;
+constexpr int kRowThreads = 1024;  // k_route_rows: 16 waves, a token each at a time
+constexpr int kRowWaves = kRowThreads / kWave;
 
-template <int VPL>
-__global__ void __launch_bounds__(kRouteThreads)
-k_route_topk(const float* __restrict__ logits, int T, int E, int k,
-             int32_t* __restrict__ ids, float* __restrict__ w) {
-  int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  int t = blockIdx.x * (kRouteThreads / kWave) + wave;
-  if (t >= T) return;
-  int id;
-  float wt;
-  float v[VPL];
-  load_logits<VPL>(logits + (size_t)t * E, E, lane, v);
-  wave_topk<VPL>(v, E, k, lane, id, wt);
-  if (lane < k) {
-    ids[(size_t)t * k + lane] = id;
-    w[(size_t)t * k + lane] = wt;
-  }
+// Chunks of whole tokens (a token's pairs never straddle two chunks), at
+// most 256 pairs each, and small enough to give about 32 chunks when there
+// are few tokens (each chunk is a workgroup of the routing kernel).
+__host__ __device__ inline int chunk_tokens(int T, int k) {
+  const int most = k >= kChunkPairs ? 1 : kChunkPairs / k;
+  const int spread = (T + 31) / 32;
+  return max(1, min(most, spread));
 }
 
-// --- histogram of one chunk of pairs -------------------------------------
-__global__ void __launch_bounds__(kRouteThreads)
-k_route_count(const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ hist) {
+int64_t route_chunks(int T, int k) {
+  const int tpc = chunk_tokens(T, k);
+  return ((int64_t)T + tpc - 1) / tpc;
+}
+
+// --- top-k and chunk histogram; (ROT) rotation of the rows in the same launch
+// Workgroups below nchunks route a chunk (a wave per token); with ROT the
+// workgroups after them rotate the token rows, 16 lanes per 128-block, with
+// the parallelism of a rotation kernel of their own (the rows do not depend
+// on the routing), so the step saves a launch without rotating on fewer CUs.
+template <int VPL, bool ROT>
+__global__ void __launch_bounds__(kRowThreads)
+k_route_rows(const float* __restrict__ logits, int T, int E, int k, int tpc, int nchunks,
+             int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ hist,
+             const uint16_t* __restrict__ x, uint16_t* __restrict__ xr, int K) {
+  if constexpr (ROT) {
+    if ((int)blockIdx.x >= nchunks) {
+      // x may be xr: each block is read whole by its 16 lanes before they write it
+      const int KB = K / kGroup, j = threadIdx.x % 16;
+      const int64_t b = (int64_t)(blockIdx.x - nchunks) * (blockDim.x / 16) + threadIdx.x / 16;
+      const bool live = b < (int64_t)T * KB;
+      const int64_t t = live ? b / KB : 0;
+      const int kb = live ? (int)(b % KB) : 0;
+      u32x4 xw = {0u, 0u, 0u, 0u};
+      if (live) xw = *reinterpret_cast<const u32x4*>(x + t * K + kb * kGroup + 8 * j);
+      const u32x4 o = fwht128_block(xw, j);   // every lane of the 16-lane row takes part
+      if (live) *reinterpret_cast<u32x4*>(xr + t * K + kb * kGroup + 8 * j) = o;
+      return;
+    }
+  }
   __shared__ int cnt[kMaxExperts];
+  __shared__ uint64_t s_rank[kRowWaves][2 * kWave];   // the threshold top-k's scratch, a wave's own
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int nwaves = blockDim.x / kWave;
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
-  int p = blockIdx.x * kChunkPairs + threadIdx.x;
-  if (p < P) atomicAdd(&cnt[ids[p]], 1);   // counts only: order does not matter
+  const int t0 = blockIdx.x * tpc, t1 = min(T, t0 + tpc);
+  for (int t = t0 + wave; t < t1; t += nwaves) {
+    float v[VPL];
+    load_logits<VPL>(logits + (size_t)t * E, E, lane, v);
+    int id;
+    float wt;
+    // the threshold top-k packs the expert index in a byte (E <= 256)
+    if constexpr (VPL <= 4) wave_topk_fast<VPL>(v, E, k, lane, id, wt, s_rank[wave]);
+    else wave_topk<VPL>(v, E, k, lane, id, wt);
+    if (lane < k) {
+      ids[(size_t)t * k + lane] = id;
+      w[(size_t)t * k + lane] = wt;
+      atomicAdd(&cnt[id], 1);   // counts only: order does not matter
+    }
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)blockIdx.x * E + e] = cnt[e];
 }
@@ -114,7 +154,7 @@ __device__ __forceinline__ int block_stable_rank(bool valid, int e, int E, int n
 
 // --- totals, scan and stable scatter of one chunk ------------------------
 __global__ void __launch_bounds__(kRouteThreads)
-k_route_scatter(const int32_t* __restrict__ ids, int P, int E, int nchunks,
+k_route_scatter(const int32_t* __restrict__ ids, int P, int E, int nchunks, int cp,
                 const int32_t* __restrict__ hist, int32_t* __restrict__ expert_off,
                 int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos) {
   __shared__ int tot[kMaxExperts];
@@ -165,8 +205,8 @@ k_route_scatter(const int32_t* __restrict__ ids, int P, int E, int nchunks,
     for (int e = threadIdx.x; e < E; e += blockDim.x) expert_off[e] = base[e];
     if (threadIdx.x == 0) expert_off[E] = P;
   }
-  int p = c * kChunkPairs + threadIdx.x;
-  bool valid = p < P;
+  int p = c * cp + threadIdx.x;          // the chunk's pairs: cp <= 256 of them
+  bool valid = (int)threadIdx.x < cp && p < P;
   int e = valid ? ids[p] : 0;
   int rank = block_stable_rank(valid, e, E, bits_for(E), wcount);
   if (valid) {
@@ -223,14 +263,12 @@ k_route_small(const float* __restrict__ logits, int T, int E, int k,
 
 size_t route_workspace_bytes(int T, int E, int k) {
   if (T <= 4) return 0;
-  size_t P = (size_t)T * k;
-  size_t nchunks = (P + kChunkPairs - 1) / kChunkPairs;
-  return nchunks * (size_t)E * sizeof(int32_t);
+  return (size_t)route_chunks(T, k) * (size_t)E * sizeof(int32_t);
 }
 
 // Scratch of the allocation-free routing call: the per-chunk histograms that
 // the caller's workspace holds otherwise. Every GPU the library runs on keeps
-// its own copy until the process ends. k_route_count rewrites every histogram
+// its own copy until the process ends. k_route_rows rewrites every histogram
 // entry a call reads, so nothing needs clearing between calls.
 static __device__ __align__(256) int32_t scratch[kRouteScratchBytes / sizeof(int32_t)];
 
@@ -272,24 +310,39 @@ hipError_t route_scratch(hipStream_t st, void** out) {
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                         int32_t* expert_off, int32_t* sorted_pairs, int32_t* pair_pos,
-                        void* ws, hipStream_t st) {
+                        void* ws, const uint16_t* x, uint16_t* xr, int K, hipStream_t st) {
   int vpl = cdiv(E, kWave);
   if (T <= 4) {
     dim3 grid(1);
     I8H_TOPK_DISPATCH(k_route_small, logits, T, E, k, ids, w, expert_off, sorted_pairs, pair_pos);
+    if (x != nullptr) return launch_fwht128(x, K, xr, K, T, K, st);
     return hipGetLastError();
   }
-  {
-    dim3 grid(cdiv(T, kRouteThreads / kWave));
-    I8H_TOPK_DISPATCH(k_route_topk, logits, T, E, k, ids, w);
-  }
-  int P = T * k;
-  int nchunks = cdiv(P, kChunkPairs);
-  if ((int64_t)nchunks * E >= ((int64_t)1 << 31)) return hipErrorInvalidValue;  // histogram index range
+  const int tpc = chunk_tokens(T, k);
+  const int64_t nchunks = route_chunks(T, k);
+  const int threads = kWave * min(kRowWaves, tpc);   // a wave per token of the chunk, at most 16
+  if (nchunks * E >= ((int64_t)1 << 31)) return hipErrorInvalidValue;  // histogram index range
   int32_t* hist = static_cast<int32_t*>(ws);
-  k_route_count<<<nchunks, kRouteThreads, 0, st>>>(ids, P, E, hist);
-  k_route_scatter<<<nchunks, kRouteThreads, 0, st>>>(ids, P, E, nchunks, hist, expert_off, sorted_pairs,
-                                                     pair_pos);
+  const int P = T * k;
+  const int nc = (int)nchunks;
+  // rotation workgroups after the routing chunks: a 128-block per 16 lanes
+  const int64_t rot_wgs = x != nullptr ? ((int64_t)T * (K / kGroup) + threads / 16 - 1) / (threads / 16) : 0;
+  if (nc + rot_wgs >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const int grid = nc + (int)rot_wgs;
+#define I8H_ROWS(V)                                                                                      \
+  do {                                                                                                   \
+    if (x != nullptr)                                                                                    \
+      k_route_rows<V, true><<<grid, threads, 0, st>>>(logits, T, E, k, tpc, nc, ids, w, hist, x, xr, K); \
+    else                                                                                                 \
+      k_route_rows<V, false><<<nc, threads, 0, st>>>(logits, T, E, k, tpc, nc, ids, w, hist, x, xr, K);  \
+  } while (0)
+  if (vpl <= 1) I8H_ROWS(1);
+  else if (vpl <= 2) I8H_ROWS(2);
+  else if (vpl <= 4) I8H_ROWS(4);
+  else if (vpl <= 8) I8H_ROWS(8);
+  else I8H_ROWS(16);
+#undef I8H_ROWS
+  k_route_scatter<<<nc, kRouteThreads, 0, st>>>(ids, P, E, nc, tpc * k, hist, expert_off, sorted_pairs, pair_pos);
   return hipGetLastError();
 }
 

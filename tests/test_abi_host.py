@@ -33,7 +33,7 @@ def L():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -85,6 +85,29 @@ def test_route_validation(L):
     # P fits in int32, but ceil(P / 256) * E (the chunk histograms' index) does not
     assert route(L, T=1 << 24, k=32, E=1024) == EUNSUP
     assert route(L, T=(1 << 24) - 8, k=32, E=1024, ptr=None) == EINVAL   # just below: other checks apply
+
+
+def test_route_rotate_validation(L):
+    f = lambda T=8, E=16, k=2, K=256, lg=A, x=A, xr=ctypes.c_void_p(0x90000), ws=A, wsb=1 << 20: \
+        L.moe_route_permute_rotate(lg, x, T, E, k, K, A, A, A, A, A, xr, ws, wsb, None)
+    assert f(K=100) == EINVAL                        # K % 128
+    assert f(K=0) == EINVAL
+    assert f(E=1025) == EUNSUP
+    assert f(E=4, k=5) == EUNSUP
+    assert f(T=0) == OK
+    assert f(x=None) == EINVAL
+    assert f(xr=None) == EINVAL
+    assert f(x=ctypes.c_void_p(0x10008)) == EINVAL   # 16-B alignment
+    assert f(xr=ctypes.c_void_p(0x10100)) == EINVAL  # partial overlap of x and x_rot
+    assert f(T=100, ws=None) == EINVAL               # workspace needed
+    assert f(T=1 << 20, K=4096) == EUNSUP            # T*K offsets are 32-bit
+    # the chunk histograms: chunks of max(1, min(floor(256 / topk), ceil(T / 32))) whole tokens
+    assert L.moe_route_permute_workspace_size(100, 16, 3) == 25 * 16 * 4    # 4 tokens a chunk
+    assert L.moe_route_permute_workspace_size(3000, 16, 3) == 36 * 16 * 4   # 85 tokens a chunk
+    assert L.moe_route_permute_workspace_size(100, 16, 32) == 25 * 16 * 4   # 4 tokens a chunk
+    assert L.moe_route_permute_workspace_size(1000, 16, 32) == 125 * 16 * 4  # 8 tokens a chunk
+    assert L.moe_route_permute_workspace_size(300, 16, 1) == 30 * 16 * 4    # 10 tokens a chunk
+    assert L.moe_route_permute_workspace_size(128, 128, 8) == 32 * 128 * 4  # verify: 4 tokens a chunk
 
 
 def test_route_noalloc_validation(L):

@@ -82,3 +82,47 @@ def test_nan_logits(gpu_available, T):
         lg[3:, ::5] = np.nan                        # NaNs in every row
         lg[5, :] = np.nan
     _run_and_compare(lg, k, nan_weights=True)
+
+
+@pytest.mark.parametrize("T,E,k,K", [(128, 128, 8, 2048), (2048, 128, 8, 2048), (3, 64, 4, 256),
+                                     (100, 96, 3, 384), (257, 300, 5, 128), (40, 1024, 32, 512),
+                                     (300, 16, 1, 256)])
+def test_route_permute_rotate(gpu_available, T, E, k, K):
+    # routing and the rotation of the routed rows in one call: the routing
+    # outputs equal the oracle's (and moe_route_permute's) bit for bit, x_rot
+    # equals hadamard128_rotate's bit for bit and the oracle's up to the proven
+    # rounding-tie window
+    from tests.gpu_util import bf16_bits_of, bf16_cuda, check_rotation
+    rng = np.random.default_rng(T * 31 + E + k + K)
+    lg = (rng.standard_normal((T, E)) + 0.5 * rng.standard_normal((1, E))).astype(np.float32)
+    xb = synth.to_bf16_bits((rng.standard_normal((T, K)) * np.where(rng.random(K) < 0.01, 20.0, 1.0))
+                            .astype(np.float32))
+    print(f"route+rotate T={T} E={E} k={k} K={K}", flush=True)
+    ref = router.route(lg, k)
+    d_lg, d_x = torch.from_numpy(lg).cuda(), bf16_cuda(xb)
+    out = i8h.moe_route_permute_rotate(d_lg, d_x, k)
+    plain = i8h.moe_route_permute(d_lg, k)
+    xr = i8h.hadamard128_rotate(d_x)
+    torch.cuda.synchronize()
+    for key in ("topk_ids", "expert_off", "sorted_pairs", "pair_pos"):
+        got = out[key].cpu().numpy()
+        assert np.array_equal(got, ref["ids" if key == "topk_ids" else key].reshape(got.shape)), key
+        assert torch.equal(out[key], plain[key]), key
+    assert torch.equal(out["topk_w"], plain["topk_w"])
+    assert_close(out["topk_w"].cpu().numpy(), ref["weights"], "topk_w")
+    assert torch.equal(out["x_rot"].view(torch.int16), xr.view(torch.int16))
+    check_rotation(xb, bf16_bits_of(out["x_rot"]))
+
+
+def test_route_permute_rotate_in_place(gpu_available):
+    from tests.gpu_util import bf16_cuda
+    rng = np.random.default_rng(77)
+    T, E, k, K = 96, 128, 8, 1024
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    xb = synth.to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
+    d_x = bf16_cuda(xb)
+    want = i8h.hadamard128_rotate(d_x)
+    out = i8h.moe_route_permute_rotate(torch.from_numpy(lg).cuda(), d_x, k, x_rot=d_x)
+    torch.cuda.synchronize()
+    assert out["x_rot"].data_ptr() == d_x.data_ptr()
+    assert torch.equal(d_x.view(torch.int16), want.view(torch.int16))
