@@ -1,7 +1,9 @@
 /*
- * i8h_probe — HBM read-bandwidth probe for measuring the library's
- * HBM-bound kernels against what a plain read reaches on the same GPU
- * (libi8h_probe.so; not part of the product path).
+ * i8h_probe — measurement probes beside the library (libi8h_probe.so; not
+ * part of the product path): an HBM read-bandwidth probe, the ceiling the
+ * HBM-bound kernels are measured against on the same GPU, and an FP8
+ * matrix-core precision probe, which runs gfx950's native E4M3 MFMA forms on
+ * caller data so that their sums can be compared with exact ones.
  */
 #ifndef I8H_PROBE_H
 #define I8H_PROBE_H
@@ -22,6 +24,23 @@ extern "C" {
  * or -3 when the HIP runtime refuses the launch. Enqueued on `stream`
  * (hipStream_t as void*). */
 int i8h_read_probe(const void* buf, size_t bytes, int blocks, uint32_t key, uint32_t* sink, void* stream);
+
+/* 32x32 MFMA with float32 accumulation on caller data, one wave per tile.
+ * form 0: v_mfma_f32_32x32x64_f8f6f4 on E4M3FN bytes (64 deep, 32 values of
+ * one byte per lane); form 1: v_mfma_f32_32x32x16_fp8_fp8 on E4M3FN bytes
+ * (16 deep, 8 per lane); form 2: v_mfma_f32_32x32x16_bf16 on bf16 values
+ * (16 deep, 8 of two bytes per lane). a, b: device arrays
+ * [tiles][steps][64 lanes][values per lane]; lane l holds row l % 32 of A
+ * (column l % 32 of B) for contraction half l / 32. c: device float32
+ * [tiles][32][32], row-major, written as
+ *   c[t][m][n] = sum over steps s, h < 2, i of
+ *                a[t][s][m + 32h][i] * b[t][s][n + 32h][i],
+ * summed by the instruction, steps accumulated in order in float32.
+ * a and b aligned to the bytes per lane (32, 8, 16), c to 4; form 0..2;
+ * tiles, steps > 0; else -1 and nothing
+ * launched. Returns 0, or -3 when the HIP runtime refuses the launch.
+ * Enqueued on `stream` (hipStream_t as void*). */
+int i8h_fp8_mfma_probe(int form, const void* a, const void* b, float* c, int tiles, int steps, void* stream);
 
 #ifdef __cplusplus
 }

@@ -272,3 +272,34 @@ def test_i8g_validation(L):
     assert q(A, 4, 128, ctypes.c_void_p(0x10004), A, None) == EINVAL            # qx needs 8-B alignment
     assert q(A, 1 << 20, 4096, A, A, None) == EUNSUP
     assert q(A, 0, 128, A, A, None) == OK
+
+
+PROBE_HEADER = os.path.join(os.path.dirname(HEADER), "i8h_probe.h")
+PROBE_LIB = os.path.join(os.path.dirname(i8h.LIB_PATH), "libi8h_probe.so")
+
+
+def test_probe_library_exports_and_validation():
+    if not os.path.exists(PROBE_LIB):
+        pytest.skip("libi8h_probe.so not built")
+    P = ctypes.CDLL(PROBE_LIB)
+    src = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b([a-z][a-z0-9_]*)\s*\(", src)) - {"defined"})
+    assert names == ["i8h_fp8_mfma_probe", "i8h_read_probe"], names
+    for n in names:
+        assert hasattr(P, n), n
+    f = P.i8h_fp8_mfma_probe
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p]
+    assert f(3, A, A, A, 1, 1, None) == -1                           # no such form
+    assert f(0, A, A, A, 0, 1, None) == -1                           # no tiles
+    assert f(0, A, A, A, 1, 0, None) == -1                           # no steps
+    assert f(0, ctypes.c_void_p(0x10010), A, A, 1, 1, None) == -1    # form 0 needs 32-B operands
+    assert f(2, A, ctypes.c_void_p(0x10008), A, 1, 1, None) == -1    # form 2 needs 16-B operands
+    assert f(1, A, A, ODD, 1, 1, None) == -1                         # c 4-B aligned
+    assert f(1, None, A, A, 1, 1, None) == -1
+    r = P.i8h_read_probe
+    r.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    assert r(A, 0, 1, 0, A, None) == -1
+    assert r(A, 24, 1, 0, A, None) == -1
+    assert r(A, 32, 0, 0, A, None) == -1
+    assert r(ODD, 32, 1, 0, A, None) == -1
