@@ -19,7 +19,7 @@ constexpr int kFwhtThreads = 256;
 constexpr int kBlocksPerWg = kFwhtThreads / 16;
 
 __global__ void __launch_bounds__(kFwhtThreads)
-k_fwht128_bf16(const uint16_t* __restrict__ x, int64_t ldx, uint16_t* __restrict__ y, int64_t ldy,
+k_fwht128_bf16(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy,   // in place allowed: not restrict
                int T, int KB) {
   int64_t hb = (int64_t)blockIdx.x * kBlocksPerWg + threadIdx.x / 16;
   int j = threadIdx.x % 16;

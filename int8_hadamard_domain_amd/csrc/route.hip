@@ -55,7 +55,7 @@ template <int VPL, bool ROT>
 __global__ void __launch_bounds__(kRowThreads)
 k_route_rows(const float* __restrict__ logits, int T, int E, int k, int tpc, int nchunks,
              int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ hist,
-             const uint16_t* __restrict__ x, uint16_t* __restrict__ xr, int K) {
+             const uint16_t* x, uint16_t* xr, int K) {   // x and xr may be one buffer: not restrict
   if constexpr (ROT) {
     if ((int)blockIdx.x >= nchunks) {
       // x may be xr: each block is read whole by its 16 lanes before they write it
