@@ -17,8 +17,8 @@ import torch
 import int8_hadamard_domain_amd as i8h
 import synth
 from oracle import gateup, hadamard, numfmt, quant, router
-from tests.gpu_util import (assert_close, bf16_bits_of, bf16_cuda, check_with_rotation_slack, fwht_tie_window,
-                             near_tie_mask)
+from tests.gpu_util import (assert_close, bf16_bits_of, bf16_cuda, check_rotation, check_with_rotation_slack,
+                            fwht_tie_window, near_tie_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -159,6 +159,33 @@ def test_full_size_sampled(gpu_available, name, path):
     rows = sample_rows(r["expert_off"], 48, seed=L.seed)
     compare(gu, act, x_rot, codes, sbits, r["expert_off"], r["sorted_pairs"], L.topk, rows=rows,
             what=f"{name}/{path}")
+
+
+@pytest.mark.parametrize("name", ["verify", "prefill"])
+def test_step_as_timed(gpu_available, name):
+    """The verify and prefill steps as the benchmark times them, at full size:
+    moe_route_permute_rotate (routing and the rotation of the token rows in
+    one launch), then the grouped product with the kernel AUTO picks. The
+    routing must match the oracle bit for bit and x_rot be the oracle's
+    rounding of the exact rotation (one bf16 step allowed where the exact
+    value sits on a rounding tie); the product on that x_rot is then held to
+    the usual tolerance on sampled rows (every expert's first and last row)."""
+    L, codes, sbits, _, r, d = full_layer(name)
+    lg = synth.router_logits(L)
+    xb = synth.activations_bf16(L)
+    print(f"gateup step as timed {name}", flush=True)
+    ro = i8h.moe_route_permute_rotate(torch.from_numpy(lg).cuda(), bf16_cuda(xb), L.topk)
+    gu, act = i8h.moe_gateup_i8h_grouped(ro["x_rot"], d["codes"], d["scales"], L.topk, ro["expert_off"],
+                                         ro["sorted_pairs"])
+    torch.cuda.synchronize()
+    for key, want in (("topk_ids", r["ids"]), ("expert_off", r["expert_off"]),
+                      ("sorted_pairs", r["sorted_pairs"]), ("pair_pos", r["pair_pos"])):
+        assert np.array_equal(ro[key].cpu().numpy(), np.asarray(want).reshape(ro[key].shape)), key
+    xr_bits = ro["x_rot"].view(torch.int16).cpu().numpy().view(np.uint16)
+    check_rotation(xb, xr_bits)
+    rows = sample_rows(r["expert_off"], 48, seed=L.seed + 1)
+    compare(gu, act, numfmt.bf16_from_bits(xr_bits), codes, sbits, r["expert_off"], r["sorted_pairs"], L.topk,
+            rows=rows, what=f"step/{name}")
 
 
 def _random_case(T, K, E, k, N, seed, code_range=127, xscale=1.0, scale_mag=4e-4):
