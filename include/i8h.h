@@ -182,7 +182,7 @@ int moe_gateup_i8h_grouped(const uint16_t* x_rot, int T, int K,
  * accumulator per 128-K group) or I8H_PATH_TALL (bf16 MFMA, passes of 256
  * pairs, the running result kept in units of the current group's scale) or
  * I8H_PATH_SKINNY (bf16 MFMA for few pairs per expert: passes of 64 pairs,
- * units of 64 gate + 64 up columns, two workgroups per CU).
+ * units of 64 gate + 64 up columns, three workgroups per CU).
  * All give the same result to float32 rounding. TALL needs N*K < 2^31
  * (else I8H_EUNSUPPORTED); its running result spans 2^64 of scale range per
  * row: a group whose scale lies more than 2^64 below the largest scale before

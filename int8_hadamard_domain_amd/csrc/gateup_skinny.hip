@@ -13,8 +13,8 @@
 // With a handful of pairs per expert the step is a stream of the touched
 // experts' codes, and what bounds it is how many bytes each CU keeps in
 // flight and how long a unit waits to fill its pipeline. So the unit is small
-// and two workgroups share a CU (one fills or drains while the other
-// streams): unit = expert e x (64 gate + the matching 64 up columns) x passes
+// and three workgroups share a CU (one fills or drains while the others
+// stream): unit = expert e x (64 gate + the matching 64 up columns) x passes
 // of 64 pairs; 4 waves, wave w takes gate columns 32 (w & 1) .. +31 and the
 // matching up columns for the m-tile w >> 1 (32 pass rows). K goes in stages
 // of 64 through a 3-slot LDS ring (A 8 KB, B 8 KB, side data 512 B a slot:
