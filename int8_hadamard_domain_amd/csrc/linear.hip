@@ -8,7 +8,13 @@
 // waves split the K groups (wave w takes g = w, w + 8, ...): more waves per
 // CU keep more loads in flight than four (6.1 against 6.5 us at the drafter
 // shape; wider workgroups, which read each activation tile fewer times, left
-// CUs idle and were slower). Per group a wave
+// CUs idle and were slower). Every workgroup reads the whole activation tile,
+// so those reads are made cheap: a wave loads its groups' 16 rows x 256 bytes
+// in whole-line pieces (four rows a load, issued before the codes), stores
+// them to a wave-private LDS tile (piece p of row r at p ^ r: the fragment
+// reads below hit 16 distinct positions) and reads its MFMA fragments from
+// there. Loading the fragments straight from global memory, 16-byte pieces
+// of 32 lines per load, took 6.1 against 5.3 us. Per group a wave
 // runs four v_mfma_f32_16x16x32_bf16 on codes decoded to bf16 (exact), from a
 // zero accumulator, then folds that group's partial into its float32 result
 // with the column's f16 scale (4 FMAs a lane). Within a group, lane quarter q
@@ -42,24 +48,38 @@ __global__ void __launch_bounds__(kLnThreads)
 k_linear_i8f16(const uint16_t* __restrict__ x, int T, int K, const int8_t* __restrict__ codes,
                const uint16_t* __restrict__ scales, int N, float* __restrict__ y) {
   __shared__ f32x4 part[kLnKS][kWave];
+  // each wave's activation tiles, one per batch slot: 16 rows x 16 pieces of 16 bytes
+  __shared__ u32x4 xs[kLnKS][kLnBatch][kLnTile][16];
   const int n0 = blockIdx.x * kLnTile, t0 = blockIdx.y * kLnTile;
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int c = lane % 16, kq = lane / 16;    // column (B) and token (A) of the lane; K quarter
   const int G = K / kGroup;
-  const int ta = t0 + c;
-  const bool tvalid = ta < T;
   const int8_t* crow = codes + (size_t)(n0 + c) * K + 32 * kq;
-  const uint16_t* xrow = x + (size_t)(tvalid ? ta : 0) * K + 32 * kq;
   const uint16_t* srow = scales + (size_t)(n0 + c) * G;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int g0 = wave; g0 < G; g0 += kLnKS * kLnBatch) {
     // every load of up to kLnBatch groups is issued before the first product:
-    // the codes (the HBM stream), then x (L2-resident) and the scales
+    // the activation rows (whole lines, into the wave's LDS tile) and the
+    // scales, then the codes (the HBM stream)
     u32x4 cv[kLnBatch][2];
     bf16x8 xa[kLnBatch][4];
     float sc[kLnBatch];
+#pragma unroll
+    for (int b = 0; b < kLnBatch; ++b) {
+      const int g = g0 + kLnKS * b;
+      if (g < G) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * j + lane / 16, pc = lane % 16;   // rows past T read as zero
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (t0 + r < T) v = *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + r) * K + (size_t)g * kGroup + 8 * pc);
+          xs[wave][b][r][pc ^ r] = v;
+        }
+        sc[b] = (float)__builtin_bit_cast(_Float16, srow[g]);
+      }
+    }
 #pragma unroll
     for (int b = 0; b < kLnBatch; ++b) {
       const int g = g0 + kLnKS * b;
@@ -68,15 +88,17 @@ k_linear_i8f16(const uint16_t* __restrict__ x, int T, int K, const int8_t* __res
         cv[b][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + (size_t)g * kGroup + 16));
       }
     }
+    // the tile is the wave's own: the wave's stores are ordered before its reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int b = 0; b < kLnBatch; ++b) {
       const int g = g0 + kLnKS * b;
       if (g < G) {
+        // MFMA i takes piece 4 kq + i of row (token) c
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          xa[b][i] = tvalid ? *reinterpret_cast<const bf16x8*>(xrow + (size_t)g * kGroup + 8 * i)
-                            : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-        sc[b] = (float)__builtin_bit_cast(_Float16, srow[g]);
+        for (int i = 0; i < 4; ++i) xa[b][i] = __builtin_bit_cast(bf16x8, xs[wave][b][c][(4 * kq + i) ^ c]);
       }
     }
 #pragma unroll
@@ -92,6 +114,10 @@ k_linear_i8f16(const uint16_t* __restrict__ x, int T, int K, const int8_t* __res
         for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc[b], p[i], acc[i]);
       }
     }
+    // the next iteration overwrites the tile: every lane's reads come first
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
   part[wave][lane] = acc;
   __syncthreads();

@@ -39,7 +39,8 @@ def quantized(n_rows, k_dim, seed):
 
 
 @pytest.mark.parametrize("T,K,N,seed", [(1, 128, 16, 0), (5, 256, 48, 1), (16, 512, 64, 2), (17, 384, 32, 3),
-                                        (33, 1024, 64, 4), (16, 4096, 256, 5), (3, 2048, 112, 6)])
+                                        (33, 1024, 64, 4), (16, 4096, 256, 5), (3, 2048, 112, 6),
+                                        (20, 2560, 48, 8)])
 def test_linear_small(T, K, N, seed):
     q, sbits = quantized(N, K, seed)
     xbits = synth.drafter_activations_bf16(T, K, seed)
