@@ -16,7 +16,14 @@
 // and three workgroups share a CU (one fills or drains while the others
 // stream): unit = expert e x (64 gate + the matching 64 up columns) x passes
 // of 64 pairs; 4 waves, wave w takes gate columns 32 (w & 1) .. +31 and the
-// matching up columns for the m-tile w >> 1 (32 pass rows). K goes in stages
+// matching up columns for the m-tile w >> 1 (32 pass rows). An expert with at
+// most 32 pairs (most of them, at a verify batch) has one m-tile, and then the
+// waves w >> 1 = 1 take k-steps 2 and 3 of every stage instead, for the same
+// columns and rows as the waves w >> 1 = 0 (k-steps 0 and 1): every wave
+// decodes half of its columns' codes, instead of two waves decoding all of
+// them while two idle, and the two partial sums of an output are added in a
+// fixed order at the end (the workgroup picks the form once, from its
+// expert's pair count, so each form is compiled on its own). K goes in stages
 // of 64 through a 3-slot LDS ring (A 8 KB, B 8 KB, side data 512 B a slot:
 // 49.5 KB a workgroup, so three share a CU) by gfx950's global -> LDS DMA,
 // two stages ahead. Each 128-K group's products accumulate from zero and are
@@ -127,7 +134,7 @@ __device__ __forceinline__ bf16x8 s_decode(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x8, p);
 }
 
-template <SFmt F>
+template <SFmt F, bool KS>
 __device__ __forceinline__ void skinny_body(const uint16_t* __restrict__ xa, const float* __restrict__ sx, int K,
                                             const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
                                             int E, int N, int k, const int32_t* __restrict__ expert_off,
@@ -194,7 +201,14 @@ __device__ __forceinline__ void skinny_body(const uint16_t* __restrict__ xa, con
 
   for (int mb = 0; mb < m_e; mb += kSRows) {
     const int rows = min(kSRows, m_e - mb);
-    const bool busy = live && rows > mw;          // the wave has live rows in this pass
+    // KS: the expert has at most 32 pairs, so this is its only pass and it
+    // has one m-tile; the waves w >> 1 = 1 then take k-steps 2 and 3 of every
+    // stage for the same columns and rows, and their partial sums join the
+    // first waves' at the end
+    constexpr bool ksplit = KS;
+    const int mt = ksplit ? 0 : mw;               // first pass row of the wave's m-tile
+    const int kh = wave >> 1;                     // with ksplit: k-steps 2 kh and 2 kh + 1
+    const bool busy = live && rows > mt;          // the wave has live rows in this pass
     // activation rows this lane copies: instruction q fills pass rows
     // 8 (2 wave + q) .. +7, lane l row + l / 8 at position l % 8; only blocks
     // holding pass rows are copied (rows past the pass repeat its last row)
@@ -251,22 +265,37 @@ __device__ __forceinline__ void skinny_body(const uint16_t* __restrict__ xa, con
       }
       // the lane's 32 codes of the stage (k = 32 half .. +31): pieces 2 half
       // and 2 half + 1 of its gate and up rows
-      u32x4 cg[2], cu[2];
+      const int m = mt + col;
+      if constexpr (KS) {
+        // k-steps 2 kh, 2 kh + 1: piece 2 half + kh of the lane's code rows
+        const u32x4 g4 = *reinterpret_cast<const u32x4*>(&bbuf[rg * kSStageK + 16 * sb_pos(rg, 2 * half + kh)]);
+        const u32x4 u4 = *reinterpret_cast<const u32x4*>(&bbuf[ru * kSStageK + 16 * sb_pos(ru, 2 * half + kh)]);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        cg[q] = *reinterpret_cast<const u32x4*>(&bbuf[rg * kSStageK + 16 * sb_pos(rg, 2 * half + q)]);
-        cu[q] = *reinterpret_cast<const u32x4*>(&bbuf[ru * kSStageK + 16 * sb_pos(ru, 2 * half + q)]);
-      }
-      const int m = mw + col;
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int s = 2 * kh + s2;
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(&abuf[m * kSStageK + 8 * sa_pos(m, 4 * half + s)]);
+          tmp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, s_decode<F>(g4[2 * s2], g4[2 * s2 + 1]), tmp[0], 0,
+                                                           0, 0);
+          tmp[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, s_decode<F>(u4[2 * s2], u4[2 * s2 + 1]), tmp[1], 0,
+                                                           0, 0);
+        }
+      } else {
+        u32x4 cg[2], cu[2];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&abuf[m * kSStageK + 8 * sa_pos(m, 4 * half + s)]);
-        const u32x4& g4 = cg[s / 2];
-        const u32x4& u4 = cu[s / 2];
-        tmp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, s_decode<F>(g4[2 * (s % 2)], g4[2 * (s % 2) + 1]),
-                                                         tmp[0], 0, 0, 0);
-        tmp[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, s_decode<F>(u4[2 * (s % 2)], u4[2 * (s % 2) + 1]),
-                                                         tmp[1], 0, 0, 0);
+        for (int q = 0; q < 2; ++q) {
+          cg[q] = *reinterpret_cast<const u32x4*>(&bbuf[rg * kSStageK + 16 * sb_pos(rg, 2 * half + q)]);
+          cu[q] = *reinterpret_cast<const u32x4*>(&bbuf[ru * kSStageK + 16 * sb_pos(ru, 2 * half + q)]);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(&abuf[m * kSStageK + 8 * sa_pos(m, 4 * half + s)]);
+          const u32x4& g4 = cg[s / 2];
+          const u32x4& u4 = cu[s / 2];
+          tmp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, s_decode<F>(g4[2 * (s % 2)], g4[2 * (s % 2) + 1]),
+                                                           tmp[0], 0, 0, 0);
+          tmp[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, s_decode<F>(u4[2 * (s % 2)], u4[2 * (s % 2) + 1]),
+                                                           tmp[1], 0, 0, 0);
+        }
       }
       if (h & 1) {
         const int g = h / 2;
@@ -281,10 +310,10 @@ __device__ __forceinline__ void skinny_body(const uint16_t* __restrict__ xa, con
         } else {
           const float wg = half_bf16(cbuf[kSRows], (par_g + g) & 1);
           const float wu = half_bf16(cbuf[kSRows + 1], (par_u + g) & 1);
-          // sx of the lane's result rows mw + 4 half + 8 (j / 4) + j % 4
+          // sx of the lane's result rows mt + 4 half + 8 (j / 4) + j % 4
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const f32x4 f = *reinterpret_cast<const f32x4*>(&cbuf[mw + 4 * half + 8 * q]);
+            const f32x4 f = *reinterpret_cast<const f32x4*>(&cbuf[mt + 4 * half + 8 * q]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               acc[0][4 * q + i] = fmaf(tmp[0][4 * q + i], wg * f[i], acc[0][4 * q + i]);
@@ -303,17 +332,37 @@ __device__ __forceinline__ void skinny_body(const uint16_t* __restrict__ xa, con
       stage(hb + 1, sA1, sB1, sC1, 0);
       stage(hb + 2, sA2, sB2, sC2, 1);
     }
-    if (busy) {
+    if constexpr (KS) {
+      // the second waves' partial sums join the first waves' (same columns,
+      // same rows) through the A slots of the ring, free once every wave is
+      // past its last stage; the next pass starts with a barrier
+      __syncthreads();
+      float* xch = reinterpret_cast<float*>(ns ? sA1 : sA0);
+      if (kh == 1 && busy) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) xch[(16 * c + j) * kWave + lane] = acc[c][j];
+      }
+      __syncthreads();
+      if (kh == 0 && busy) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) acc[c][j] += xch[(16 * c + j) * kWave + lane];
+      }
+    }
+    if (busy && !(ksplit && kh == 1)) {
       // uniform bases and 32-bit lane offsets, opaque so the compiler does
       // not hoist the store addresses of every pass out of the pass loop
       float* act_b = act ? act + (size_t)(r0 + mb) * I : nullptr;
       float* gu_b = gu ? gu + (size_t)(r0 + mb) * N : nullptr;
-      uint32_t go = (uint32_t)((mw + 4 * half) * N + i0 + col), ao = (uint32_t)((mw + 4 * half) * I + i0 + col);
+      uint32_t go = (uint32_t)((mt + 4 * half) * N + i0 + col), ao = (uint32_t)((mt + 4 * half) * I + i0 + col);
       asm volatile("" : "+v"(go), "+v"(ao));
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int dm = 8 * (j / 4) + (j % 4);
-        if (mw + 4 * half + dm < rows) {
+        if (mt + 4 * half + dm < rows) {
           const float gv = acc[0][j], uv = acc[1][j];
           if (gu_b) {
             gu_b[go + (uint32_t)(dm * N)] = gv;
@@ -326,12 +375,24 @@ __device__ __forceinline__ void skinny_body(const uint16_t* __restrict__ xa, con
   }
 }
 
+// the block's expert has 1..32 pairs (one pass with one m-tile): the split form
+__device__ __forceinline__ bool skinny_split(int E, const int32_t* __restrict__ expert_off, int ntiles) {
+  const int slot = blockIdx.x / kSXcds;
+  const int e = (blockIdx.x % kSXcds) + kSXcds * (slot / ntiles);
+  if (e >= E) return false;
+  const int m_e = expert_off[e + 1] - expert_off[e];
+  return m_e <= 32;
+}
+
 __global__ void __launch_bounds__(kSThreads, 3)
 k_gateup_i8h_skinny(const uint16_t* __restrict__ xa, int K, const uint8_t* __restrict__ codes,
                     const uint16_t* __restrict__ scales, int E, int N, int k,
                     const int32_t* __restrict__ expert_off, const int32_t* __restrict__ sorted_pairs,
                     float* __restrict__ gu, float* __restrict__ act, int ntiles) {
-  skinny_body<SFmt::I8>(xa, nullptr, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu, act, ntiles);
+  if (skinny_split(E, expert_off, ntiles))
+    skinny_body<SFmt::I8, true>(xa, nullptr, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu, act, ntiles);
+  else
+    skinny_body<SFmt::I8, false>(xa, nullptr, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu, act, ntiles);
 }
 
 __global__ void __launch_bounds__(kSThreads, 3)
@@ -339,7 +400,10 @@ k_gateup_fp8_skinny(const uint16_t* __restrict__ xq, const float* __restrict__ s
                     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int E, int N, int k,
                     const int32_t* __restrict__ expert_off, const int32_t* __restrict__ sorted_pairs,
                     float* __restrict__ gu, float* __restrict__ act, int ntiles) {
-  skinny_body<SFmt::E4M3>(xq, sx, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu, act, ntiles);
+  if (skinny_split(E, expert_off, ntiles))
+    skinny_body<SFmt::E4M3, true>(xq, sx, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu, act, ntiles);
+  else
+    skinny_body<SFmt::E4M3, false>(xq, sx, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu, act, ntiles);
 }
 
 }  // namespace
