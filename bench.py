@@ -78,6 +78,9 @@ def parse():
                     help="rotate with hadamard128_rotate as a call of its own, then moe_gateup_i8h_grouped "
                          "(defaults: decode rotates inside the gate_up kernel, many tokens inside the routing "
                          "kernel, moe_route_permute_rotate)")
+    ap.add_argument("--act-f32", action="store_true",
+                    help="--stage down: float32 act rows, rounded to bf16 inside the call (default: bf16 rows, "
+                         "as the gate_up calls' bf16 form hands them over)")
     ap.add_argument("--stage", default="gate_up", choices=["gate_up", "down", "linear"],
                     help="down: time the step after the path instead, moe_down_bf16_combine (bf16 grouped down "
                          "projection + weighted combine) on the workload's token count, with the routing "
@@ -518,7 +521,9 @@ def measured_traffic(key, workload):
 
 def bench_down(args, L, dev):
     """The step after the path on the workload's shapes: out[T, H] from the
-    expert-sorted act rows [P, I] float32 and W_down [E, H, I] bf16 (H = K)."""
+    expert-sorted act rows [P, I] and W_down [E, H, I] bf16 (H = K). The act
+    rows come in bf16, as the gate_up calls hand them over in their bf16 form
+    (--act-f32: float32 rows, rounded inside the call)."""
     import torch
     import int8_hadamard_domain_amd as i8h
     import synth
@@ -540,9 +545,13 @@ def bench_down(args, L, dev):
     ws_ = [w0] + [w0.clone() for _ in range(copies - 1)]
     act_np = synth.act_f32(LB).reshape(nb, L.P, I)
     acts = torch.from_numpy(act_np).to(dev)
+    act16 = not args.act_f32
+    if act16:
+        acts = acts.to(torch.bfloat16)
     routes = [i8h.moe_route_permute(torch.from_numpy(logits_np[b]).to(dev), k) for b in range(nb)]
     out = torch.empty((L.T, H), dtype=torch.float32, device=dev)
-    wsz = i8h.lib().moe_down_bf16_workspace_size(L.T, I, H, k)
+    wsz = (i8h.lib().moe_down_bf16_act_bf16_workspace_size if act16 else
+           i8h.lib().moe_down_bf16_workspace_size)(L.T, I, H, k)
     work = torch.empty((max(wsz, 1),), dtype=torch.uint8, device=dev)
     gemv = L.P <= 64
 
@@ -558,14 +567,16 @@ def bench_down(args, L, dev):
     call_us = step_ms_ev * 1e3
     value = wbytes.mean() * steps / wall / 1e9
     # algorithmic bytes per call: touched W_down, act read once, out written, routing lists
-    alg = wbytes.mean() + L.P * I * 4 + L.T * H * 4 + L.P * 4 * 3 + (L.E + 1) * 4
+    alg = wbytes.mean() + L.P * I * (2 if act16 else 4) + L.T * H * 4 + L.P * 4 * 3 + (L.E + 1) * 4
     achieved = alg / (call_us * 1e-6) / 1e9
     flops = 2.0 * L.P * H * I
     key = "down_gemv" if gemv else "down_gemm"
     kernel = ("k_down_gemv_combine (one launch)" if gemv else
+              "k_down_gemm + k_down_combine (the call)" if act16 else
               "k_f32_to_bf16 + k_down_gemm + k_down_combine (the call)")
+    workload = "down-" + L.name + ("" if act16 else "-f32act")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(key, "down-" + L.name),
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(key, workload),
                 "kernel": kernel, "kernel_us": round(call_us, 3), "alg_bytes_per_launch": int(alg),
                 "mfma_tflops": round(flops / (call_us * 1e-6) / 1e12, 2)}
 
@@ -606,12 +617,14 @@ def bench_down(args, L, dev):
         "vs_baseline": None,
         "dtype": "bf16*bf16->f32",
         "data": "synthetic",
-        "config": {"workload": f"down-{L.name}: T={L.T} H={H} I={I} E={L.E} top-{k} (down projection + "
+        "config": {"workload": f"{workload}: T={L.T} H={H} I={I} E={L.E} top-{k} (down projection + "
                                f"combine of Gemma 4 26B-A4B)",
                    "T": L.T, "H": H, "I": I, "E": L.E, "topk": k, "weight_copies": int(copies),
                    "steps_per_graph": int(S), "touched_experts_per_step": float(np.mean(touched)),
                    "setup_s": round(setup_s, 1),
-                   "step": "moe_down_bf16_combine (" + ("one launch" if gemv else "bf16 act, GEMM, combine") + ")"},
+                   "act": "bf16" if act16 else "float32",
+                   "step": "moe_down_bf16_combine (" + ("one launch" if gemv else "GEMM, combine" if act16 else
+                                                       "bf16 act, GEMM, combine") + ")"},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }))

@@ -196,6 +196,18 @@ int moe_gateup_i8h_grouped_path(const uint16_t* x_rot, int T, int K,
                                 const int32_t* expert_off, const int32_t* sorted_pairs,
                                 float* gate_up, float* act, int path, void* stream);
 
+/* moe_gateup_i8h_grouped_path with act stored in bf16, the input the bf16
+ * down projection takes (moe_down_bf16_combine_act_bf16): act_bf16
+ * [T*topk, N/2] bf16 bits out, 2-B aligned, or NULL. Each value is the
+ * float32 act of moe_gateup_i8h_grouped_path rounded to nearest even, so it
+ * equals that call's act rounded the way the down projection rounds it;
+ * gate_up stays float32. Same paths, limits and status codes. */
+int moe_gateup_i8h_grouped_act_bf16(const uint16_t* x_rot, int T, int K,
+                                    const int8_t* codes, const uint16_t* scales,
+                                    int E, int N, int topk,
+                                    const int32_t* expert_off, const int32_t* sorted_pairs,
+                                    float* gate_up, uint16_t* act_bf16, int path, void* stream);
+
 /* Same product with the rotation fused in: x is the UNROTATED bf16
  * activation [T, K]. The 128-wide Walsh-Hadamard rotation of
  * hadamard128_rotate is applied on the fly (the int8 card's model table, row
@@ -286,6 +298,17 @@ int moe_gateup_fp8blk_grouped_path(const uint16_t* x, int T, int K,
                                    void* workspace, size_t workspace_bytes, int path,
                                    void* stream);
 
+/* moe_gateup_fp8blk_grouped_path with act stored in bf16 (act_bf16
+ * [T*topk, N/2] bf16 bits out, 2-B aligned, or NULL): each value the float32
+ * act rounded to nearest even, as for moe_gateup_i8h_grouped_act_bf16. */
+int moe_gateup_fp8blk_grouped_act_bf16(const uint16_t* x, int T, int K,
+                                       const uint8_t* codes, const uint16_t* scales,
+                                       int E, int N, int topk,
+                                       const int32_t* expert_off, const int32_t* sorted_pairs,
+                                       float* gate_up, uint16_t* act_bf16,
+                                       void* workspace, size_t workspace_bytes, int path,
+                                       void* stream);
+
 /* ------------------------------------------------------------------------
  * The step after the path: bf16 grouped down projection of the routed
  * experts, then the weighted combine of each token's topk outputs.
@@ -329,6 +352,21 @@ int moe_down_bf16_combine_path(const float* act, int T, int I, const uint16_t* w
                                const int32_t* expert_off, const int32_t* pair_pos,
                                float* out, void* workspace, size_t workspace_bytes,
                                int path, void* stream);
+
+/* moe_down_bf16_combine_path on act already in bf16 (act_bf16 [P, I] bf16
+ * bits, 16-B aligned, as moe_gateup_*_act_bf16 write it): the rounding step
+ * is skipped, and the GEMM form reads act_bf16 directly, so its workspace
+ * holds y only: at least moe_down_bf16_act_bf16_workspace_size(T, I, H, topk)
+ * bytes, 256-B aligned (unused, may be NULL, for the one-launch form). Same
+ * forms, limits and status codes; on act_bf16 = bf16(act) the results equal
+ * moe_down_bf16_combine_path's on act bit for bit. */
+size_t moe_down_bf16_act_bf16_workspace_size(int T, int I, int H, int topk);
+int moe_down_bf16_combine_act_bf16(const uint16_t* act_bf16, int T, int I, const uint16_t* w_down,
+                                   int E, int H, int topk,
+                                   const int32_t* topk_ids, const float* topk_w,
+                                   const int32_t* expert_off, const int32_t* pair_pos,
+                                   float* out, void* workspace, size_t workspace_bytes,
+                                   int path, void* stream);
 
 /* ------------------------------------------------------------------------
  * Dense int8 linear with an f16 scale per row and 128 of K, no transform: the
@@ -380,6 +418,16 @@ int moe_gateup_i8g_grouped(const uint16_t* x, int T, int K,
                            const int32_t* expert_off, const int32_t* sorted_pairs,
                            float* gate_up, float* act,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_gateup_i8g_grouped with act stored in bf16 (act_bf16 [T*topk, N/2] bf16
+ * bits out, 2-B aligned, or NULL): each value the float32 act rounded to
+ * nearest even, as for moe_gateup_i8h_grouped_act_bf16. */
+int moe_gateup_i8g_grouped_act_bf16(const uint16_t* x, int T, int K,
+                                    const int8_t* codes, const uint16_t* scales,
+                                    int E, int N, int topk,
+                                    const int32_t* expert_off, const int32_t* sorted_pairs,
+                                    float* gate_up, uint16_t* act_bf16,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -65,6 +65,7 @@ def lib():
         "hadamard128_rotate": (I, [P, I64, P, I64, I, I, P]),
         "moe_gateup_i8h_grouped": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P]),
         "moe_gateup_i8h_grouped_path": (I, [P, I, I, P, P, I, I, I, P, P, P, P, I, P]),
+        "moe_gateup_i8h_grouped_act_bf16": (I, [P, I, I, P, P, I, I, I, P, P, P, P, I, P]),
         "moe_gateup_i8h_fused_workspace_size": (SZ, [I, I]),
         "moe_gateup_i8h_grouped_fused": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P, SZ, P]),
         "moe_route_gateup_i8h_decode": (I, [P, P, I, I, P, P, I, I, I, P, P, P, P, P, P, P, P]),
@@ -72,12 +73,16 @@ def lib():
         "moe_gateup_fp8blk_workspace_size": (SZ, [I, I]),
         "moe_gateup_fp8blk_grouped": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P, SZ, P]),
         "moe_gateup_fp8blk_grouped_path": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P, SZ, I, P]),
+        "moe_gateup_fp8blk_grouped_act_bf16": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P, SZ, I, P]),
         "i8_quantize_activations": (I, [P, I, I, P, P, P]),
         "moe_gateup_i8g_workspace_size": (SZ, [I, I]),
         "moe_gateup_i8g_grouped": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P, SZ, P]),
+        "moe_gateup_i8g_grouped_act_bf16": (I, [P, I, I, P, P, I, I, I, P, P, P, P, P, SZ, P]),
         "moe_down_bf16_workspace_size": (SZ, [I, I, I, I]),
         "moe_down_bf16_combine": (I, [P, I, I, P, I, I, I, P, P, P, P, P, P, SZ, P]),
         "moe_down_bf16_combine_path": (I, [P, I, I, P, I, I, I, P, P, P, P, P, P, SZ, I, P]),
+        "moe_down_bf16_act_bf16_workspace_size": (SZ, [I, I, I, I]),
+        "moe_down_bf16_combine_act_bf16": (I, [P, I, I, P, I, I, I, P, P, P, P, P, P, SZ, I, P]),
         "linear_i8f16": (I, [P, I, I, P, P, I, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -213,14 +218,17 @@ def hadamard128_rotate(x, out=None):
 
 
 def moe_gateup_i8h_grouped(x_rot, codes, scales, topk, expert_off, sorted_pairs,
-                           gate_up=True, act=True, path="auto"):
+                           gate_up=True, act=True, path="auto", act_dtype=torch.float32):
     """Grouped int8 Hadamard-domain gate_up.
 
     x_rot [T, K] bf16 (rotated), codes [E, N, K] int8, scales [E, N, K/128]
     bf16, expert_off [E+1] / sorted_pairs [T*topk] int32 from
     moe_route_permute. gate_up / act: True to allocate, a tensor to write
-    into, or False/None to skip. Returns (gate_up, act) in expert-sorted
-    row order (None for skipped outputs).
+    into, or False/None to skip. act is float32, or bfloat16 (act_dtype, or
+    the dtype of a given tensor: each value rounded to nearest even from the
+    float32 one, the input moe_down_bf16_combine takes without rounding it
+    again). Returns (gate_up, act) in expert-sorted row order (None for
+    skipped outputs).
     """
     _dev(x_rot, "x_rot", torch.bfloat16, 2)
     T, K = x_rot.shape
@@ -232,8 +240,10 @@ def moe_gateup_i8h_grouped(x_rot, codes, scales, topk, expert_off, sorted_pairs,
     _dev(expert_off, "expert_off", torch.int32, shape=(E + 1,), device=dev)
     _dev(sorted_pairs, "sorted_pairs", torch.int32, shape=(T * topk,), device=dev)
     gu = _out(gate_up, (T * topk, N), dev)
-    ac = _out(act, (T * topk, N // 2), dev)
-    _check("moe_gateup_i8h_grouped", lib().moe_gateup_i8h_grouped_path(
+    adt = _act_dtype(act, act_dtype)
+    ac = _out(act, (T * topk, N // 2), dev, adt)
+    fn = "moe_gateup_i8h_grouped_act_bf16" if adt == torch.bfloat16 else "moe_gateup_i8h_grouped_path"
+    _check(fn, getattr(lib(), fn)(
         _ptr(x_rot), T, K, _ptr(codes), _ptr(scales), E, N, topk, _ptr(expert_off), _ptr(sorted_pairs),
         _ptr(gu), _ptr(ac), PATHS[path], _stream(dev)))
     return gu, ac
@@ -289,12 +299,20 @@ def moe_route_gateup_i8h_decode(logits, x, codes, scales, topk, gate_up=True, ac
     return o, gu, ac
 
 
-def _out(spec, shape, dev):
+def _out(spec, shape, dev, dtype=torch.float32):
     if spec is None or spec is False:
         return None
     if spec is True:
-        return torch.empty(shape, dtype=torch.float32, device=dev)
-    return _dev(spec, "output", torch.float32, shape=shape, device=dev)
+        return torch.empty(shape, dtype=dtype, device=dev)
+    return _dev(spec, "output", dtype, shape=shape, device=dev)
+
+
+def _act_dtype(act, act_dtype):
+    """The act output's dtype: a given tensor's own, else act_dtype (float32 or bfloat16)."""
+    dt = act.dtype if isinstance(act, torch.Tensor) else act_dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"act must be float32 or bfloat16 (got {dt})")
+    return dt
 
 
 def fp8_quantize_activations(x, qx=None, sx=None):
@@ -312,13 +330,14 @@ def fp8_quantize_activations(x, qx=None, sx=None):
 
 
 def moe_gateup_fp8blk_grouped(x, codes, scales, topk, expert_off, sorted_pairs,
-                              gate_up=True, act=True, workspace=None, path="auto"):
+                              gate_up=True, act=True, workspace=None, path="auto", act_dtype=torch.float32):
     """Grouped FP8 E4M3 128x128-block gate_up.
 
     x [T, K] bf16 (not rotated), codes [E, N, K] uint8 (E4M3 bytes), scales
-    [E, N/128, K/128] bf16. path: "auto", "gemm" or "skinny". Returns
-    (gate_up, act, workspace); the workspace holds the quantized activations
-    (see fp8_workspace_views).
+    [E, N/128, K/128] bf16. path: "auto", "gemm" or "skinny". act float32 or
+    bfloat16 as for moe_gateup_i8h_grouped. Returns (gate_up, act,
+    workspace); the workspace holds the quantized activations (see
+    fp8_workspace_views).
     """
     _dev(x, "x", torch.bfloat16, 2)
     T, K = x.shape
@@ -332,8 +351,10 @@ def moe_gateup_fp8blk_grouped(x, codes, scales, topk, expert_off, sorted_pairs,
     need = lib().moe_gateup_fp8blk_workspace_size(T, K)
     workspace = _workspace(workspace, "workspace", need, dev)
     gu = _out(gate_up, (T * topk, N), dev)
-    ac = _out(act, (T * topk, N // 2), dev)
-    _check("moe_gateup_fp8blk_grouped", lib().moe_gateup_fp8blk_grouped_path(
+    adt = _act_dtype(act, act_dtype)
+    ac = _out(act, (T * topk, N // 2), dev, adt)
+    fn = "moe_gateup_fp8blk_grouped_act_bf16" if adt == torch.bfloat16 else "moe_gateup_fp8blk_grouped_path"
+    _check(fn, getattr(lib(), fn)(
         _ptr(x), T, K, _ptr(codes), _ptr(scales), E, N, topk, _ptr(expert_off), _ptr(sorted_pairs),
         _ptr(gu), _ptr(ac), _ptr(workspace), workspace.numel(), PATHS[path], _stream(dev)))
     return gu, ac, workspace
@@ -354,12 +375,16 @@ def fp8_workspace_views(workspace, T, K):
 
 def moe_down_bf16_combine(act, w_down, routing, out=None, workspace=None, path="auto"):
     """bf16 grouped down projection of the expert-sorted act rows [P, I]
-    float32 (rounded to bf16 for the product) against w_down [E, H, I] bf16,
-    merged per token with the router weights: returns out [T, H] float32.
+    float32 (rounded to bf16 for the product), or bfloat16 (taken as they
+    are: the gate_up calls' bf16 act), against w_down [E, H, I] bf16, merged
+    per token with the router weights: returns out [T, H] float32.
     `routing` is moe_route_permute's dict (topk_ids, topk_w, expert_off,
     pair_pos); `path` is "auto", "gemv" (one launch) or "gemm" (GEMM +
     combine)."""
-    _dev(act, "act", torch.float32, 2)
+    if not isinstance(act, torch.Tensor) or act.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("act must be a float32 or bfloat16 tensor")
+    bf = act.dtype == torch.bfloat16
+    _dev(act, "act", act.dtype, 2)
     P, I = act.shape
     dev = act.device
     _dev(w_down, "w_down", torch.bfloat16, 3, device=dev)
@@ -372,14 +397,15 @@ def moe_down_bf16_combine(act, w_down, routing, out=None, workspace=None, path="
     tw = _dev(routing["topk_w"], "topk_w", torch.float32, shape=(T, topk), device=dev)
     off = _dev(routing["expert_off"], "expert_off", torch.int32, shape=(E + 1,), device=dev)
     pos = _dev(routing["pair_pos"], "pair_pos", torch.int32, shape=(P,), device=dev)
-    need = lib().moe_down_bf16_workspace_size(T, I, H, topk)
+    need = (lib().moe_down_bf16_act_bf16_workspace_size if bf else lib().moe_down_bf16_workspace_size)(T, I, H, topk)
     if path != "gemv" or workspace is not None:
         workspace = _workspace(workspace, "workspace", need, dev)
     if out is None:
         out = torch.empty((T, H), dtype=torch.float32, device=dev)
     else:
         _dev(out, "out", torch.float32, shape=(T, H), device=dev)
-    _check("moe_down_bf16_combine", lib().moe_down_bf16_combine_path(
+    fn = "moe_down_bf16_combine_act_bf16" if bf else "moe_down_bf16_combine_path"
+    _check(fn, getattr(lib(), fn)(
         _ptr(act), T, I, _ptr(w_down), E, H, topk, _ptr(ids), _ptr(tw), _ptr(off), _ptr(pos), _ptr(out),
         _ptr(workspace), 0 if workspace is None else workspace.numel(), DOWN_PATHS[path], _stream(dev)))
     return out
@@ -415,12 +441,13 @@ def i8_quantize_activations(x):
 
 
 def moe_gateup_i8g_grouped(x, codes, scales, topk, expert_off, sorted_pairs,
-                           gate_up=True, act=True, workspace=None):
+                           gate_up=True, act=True, workspace=None, act_dtype=torch.float32):
     """Grouped W8A8 int8 g128 gate_up.
 
     x [T, K] bf16 (not rotated), codes [E, N, K] int8, scales [E, N, K/128]
-    bf16. Returns (gate_up, act, workspace); the workspace holds the int8
-    activations and their scales (see i8g_workspace_views).
+    bf16. act float32 or bfloat16 as for moe_gateup_i8h_grouped. Returns
+    (gate_up, act, workspace); the workspace holds the int8 activations and
+    their scales (see i8g_workspace_views).
     """
     _dev(x, "x", torch.bfloat16, 2)
     T, K = x.shape
@@ -434,8 +461,10 @@ def moe_gateup_i8g_grouped(x, codes, scales, topk, expert_off, sorted_pairs,
     need = lib().moe_gateup_i8g_workspace_size(T, K)
     workspace = _workspace(workspace, "workspace", need, dev)
     gu = _out(gate_up, (T * topk, N), dev)
-    ac = _out(act, (T * topk, N // 2), dev)
-    _check("moe_gateup_i8g_grouped", lib().moe_gateup_i8g_grouped(
+    adt = _act_dtype(act, act_dtype)
+    ac = _out(act, (T * topk, N // 2), dev, adt)
+    fn = "moe_gateup_i8g_grouped_act_bf16" if adt == torch.bfloat16 else "moe_gateup_i8g_grouped"
+    _check(fn, getattr(lib(), fn)(
         _ptr(x), T, K, _ptr(codes), _ptr(scales), E, N, topk, _ptr(expert_off), _ptr(sorted_pairs),
         _ptr(gu), _ptr(ac), _ptr(workspace), workspace.numel(), _stream(dev)))
     return gu, ac, workspace

@@ -43,9 +43,10 @@ inline int auto_path(int T, int K, int E, int N, int topk) {
   return I8H_PATH_SKINNY;
 }
 
+// act: float32 [P, I], or bf16 [P, I] when act_bf16
 int gateup_i8h(const uint16_t* x_rot, int T, int K, const int8_t* codes, const uint16_t* scales, int E, int N,
-               int topk, const int32_t* expert_off, const int32_t* sorted_pairs, float* gate_up, float* act,
-               int path, void* stream) {
+               int topk, const int32_t* expert_off, const int32_t* sorted_pairs, float* gate_up, void* act,
+               bool act_bf16, int path, void* stream) {
   int rc = check_common_moe(T, K, E, N, topk);
   if (rc != I8H_OK) return rc;
   if ((N % 2) != 0) return I8H_EINVAL;                  // gate and up halves
@@ -55,7 +56,7 @@ int gateup_i8h(const uint16_t* x_rot, int T, int K, const int8_t* codes, const u
   if (!x_rot || !codes || !scales || !expert_off || !sorted_pairs) return I8H_EINVAL;
   if (!aligned(x_rot, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return I8H_EINVAL;
   if (!aligned(expert_off, 4) || !aligned(sorted_pairs, 4)) return I8H_EINVAL;
-  if ((gate_up && !aligned(gate_up, 4)) || (act && !aligned(act, 4))) return I8H_EINVAL;
+  if ((gate_up && !aligned(gate_up, 4)) || (act && !aligned(act, act_bf16 ? 2 : 4))) return I8H_EINVAL;
   if (!gate_up && !act) return I8H_OK;  // nothing requested
   if (path == I8H_PATH_GEMV && K > kGemvMaxK) return I8H_EUNSUPPORTED;
   if (path == I8H_PATH_TALL && !tall_fits(K, N)) return I8H_EUNSUPPORTED;
@@ -63,16 +64,16 @@ int gateup_i8h(const uint16_t* x_rot, int T, int K, const int8_t* codes, const u
   hipError_t e;
   if (path == I8H_PATH_GEMV)
     e = i8h::launch_gateup_i8h_gemv(x_rot, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up,
-                                    act, as_stream(stream));
+                                    act, act_bf16, as_stream(stream));
   else if (path == I8H_PATH_TALL)
     e = i8h::launch_gateup_i8h_gemm_tall(x_rot, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs,
-                                         gate_up, act, as_stream(stream));
+                                         gate_up, act, act_bf16, as_stream(stream));
   else if (path == I8H_PATH_SKINNY)
     e = i8h::launch_gateup_i8h_skinny(x_rot, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up,
-                                      act, as_stream(stream));
+                                      act, act_bf16, as_stream(stream));
   else
     e = i8h::launch_gateup_i8h_gemm(x_rot, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up,
-                                    act, as_stream(stream));
+                                    act, act_bf16, as_stream(stream));
   return from_hip(e);
 }
 
@@ -118,7 +119,8 @@ struct DownWs {
   }
 };
 
-int down_combine(const float* act, int T, int I, const uint16_t* w_down, int E, int H, int topk,
+// act: float32 [P, I], or bf16 [P, I] when act_bf16 (then the workspace holds y only)
+int down_combine(const void* act, bool act_bf16, int T, int I, const uint16_t* w_down, int E, int H, int topk,
                  const int32_t* topk_ids, const float* topk_w, const int32_t* expert_off, const int32_t* pair_pos,
                  float* out, void* workspace, size_t workspace_bytes, int path, void* stream) {
   if (T < 0 || I <= 0 || (I % 8) != 0 || H <= 0 || (H % 8) != 0 || E <= 0 || topk <= 0) return I8H_EINVAL;
@@ -139,16 +141,18 @@ int down_combine(const float* act, int T, int I, const uint16_t* w_down, int E, 
   }
   if (path == I8H_DOWN_GEMV) {
     if (!down_gemv_ok(I, H)) return I8H_EUNSUPPORTED;
-    return from_hip(i8h::launch_down_gemv_combine(act, T, I, w_down, H, topk, topk_ids, topk_w, pair_pos, out,
-                                                  as_stream(stream)));
+    return from_hip(i8h::launch_down_gemv_combine(act, act_bf16, T, I, w_down, H, topk, topk_ids, topk_w, pair_pos,
+                                                  out, as_stream(stream)));
   }
   if (!down_gemm_ok(T, I, H, topk)) return I8H_EUNSUPPORTED;
   const DownWs ws(T, I, H, topk);
-  if (!workspace || workspace_bytes < ws.total || !aligned(workspace, 256)) return I8H_EINVAL;
+  const size_t need = act_bf16 ? ws.y : ws.total;
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return I8H_EINVAL;
   uint8_t* base = static_cast<uint8_t*>(workspace);
-  return from_hip(i8h::launch_down_gemm_combine(act, T, I, w_down, E, H, topk, topk_w, expert_off, pair_pos,
-                                                reinterpret_cast<uint16_t*>(base),
-                                                reinterpret_cast<float*>(base + ws.a16), out, as_stream(stream)));
+  uint16_t* a16 = act_bf16 ? nullptr : reinterpret_cast<uint16_t*>(base);
+  float* y = reinterpret_cast<float*>(act_bf16 ? base : base + ws.a16);
+  return from_hip(i8h::launch_down_gemm_combine(act, act_bf16, T, I, w_down, E, H, topk, topk_w, expert_off,
+                                                pair_pos, a16, y, out, as_stream(stream)));
 }
 
 }  // namespace
@@ -255,15 +259,23 @@ int hadamard128_rotate(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy,
 int moe_gateup_i8h_grouped(const uint16_t* x_rot, int T, int K, const int8_t* codes, const uint16_t* scales, int E,
                            int N, int topk, const int32_t* expert_off, const int32_t* sorted_pairs,
                            float* gate_up, float* act, void* stream) {
-  return gateup_i8h(x_rot, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up, act,
+  return gateup_i8h(x_rot, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up, act, false,
                     I8H_PATH_AUTO, stream);
 }
 
 int moe_gateup_i8h_grouped_path(const uint16_t* x_rot, int T, int K, const int8_t* codes, const uint16_t* scales,
                                 int E, int N, int topk, const int32_t* expert_off, const int32_t* sorted_pairs,
                                 float* gate_up, float* act, int path, void* stream) {
-  return gateup_i8h(x_rot, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up, act, path,
+  return gateup_i8h(x_rot, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up, act, false, path,
                     stream);
+}
+
+int moe_gateup_i8h_grouped_act_bf16(const uint16_t* x_rot, int T, int K, const int8_t* codes,
+                                    const uint16_t* scales, int E, int N, int topk, const int32_t* expert_off,
+                                    const int32_t* sorted_pairs, float* gate_up, uint16_t* act_bf16, int path,
+                                    void* stream) {
+  return gateup_i8h(x_rot, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up, act_bf16, true,
+                    path, stream);
 }
 
 int fp8_quantize_activations(const uint16_t* x, int T, int K, uint8_t* qx, float* sx, void* stream) {
@@ -307,9 +319,9 @@ int moe_gateup_i8h_grouped_fused(const uint16_t* x, int T, int K, const int8_t* 
   if (i8h::launch_fwht128(x, K, xr, K, T, K, st) != hipSuccess) return I8H_EHIP;
   if (auto_path(T, K, E, N, topk) == I8H_PATH_TALL)
     return from_hip(i8h::launch_gateup_i8h_gemm_tall(xr, T, K, codes, scales, E, N, topk, expert_off,
-                                                      sorted_pairs, gate_up, act, st));
+                                                      sorted_pairs, gate_up, act, false, st));
   return from_hip(i8h::launch_gateup_i8h_skinny(xr, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs,
-                                                gate_up, act, st));
+                                                gate_up, act, false, st));
 }
 
 int moe_route_gateup_i8h_decode(const float* logits, const uint16_t* x, int T, int K, const int8_t* codes,
@@ -335,10 +347,14 @@ int moe_route_gateup_i8h_decode(const float* logits, const uint16_t* x, int T, i
                                                   as_stream(stream)));
 }
 
-int moe_gateup_fp8blk_grouped_path(const uint16_t* x, int T, int K, const uint8_t* codes, const uint16_t* scales,
-                                   int E, int N, int topk, const int32_t* expert_off, const int32_t* sorted_pairs,
-                                   float* gate_up, float* act, void* workspace, size_t workspace_bytes, int path,
-                                   void* stream) {
+}  // extern "C"
+
+namespace {
+
+// act: float32 [P, I], or bf16 [P, I] when act_bf16
+int gateup_fp8(const uint16_t* x, int T, int K, const uint8_t* codes, const uint16_t* scales, int E, int N,
+               int topk, const int32_t* expert_off, const int32_t* sorted_pairs, float* gate_up, void* act,
+               bool act_bf16, void* workspace, size_t workspace_bytes, int path, void* stream) {
   int rc = check_common_moe(T, K, E, N, topk);
   if (rc != I8H_OK) return rc;
   if ((N % 128) != 0) return I8H_EINVAL;
@@ -349,7 +365,7 @@ int moe_gateup_fp8blk_grouped_path(const uint16_t* x, int T, int K, const uint8_
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(expert_off, 4) ||
       !aligned(sorted_pairs, 4))
     return I8H_EINVAL;
-  if ((gate_up && !aligned(gate_up, 4)) || (act && !aligned(act, 4))) return I8H_EINVAL;
+  if ((gate_up && !aligned(gate_up, 4)) || (act && !aligned(act, act_bf16 ? 2 : 4))) return I8H_EINVAL;
   size_t need = moe_gateup_fp8blk_workspace_size(T, K);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return I8H_EINVAL;
   if (!gate_up && !act) return I8H_OK;
@@ -366,9 +382,29 @@ int moe_gateup_fp8blk_grouped_path(const uint16_t* x, int T, int K, const uint8_
   if (e != hipSuccess) return I8H_EHIP;
   if (path == I8H_PATH_SKINNY)
     return from_hip(i8h::launch_gateup_fp8_skinny(xq, sx, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs,
-                                                  gate_up, act, st));
+                                                  gate_up, act, act_bf16, st));
   return from_hip(i8h::launch_gateup_fp8(xq, sx, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs,
-                                         gate_up, act, st));
+                                         gate_up, act, act_bf16, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_gateup_fp8blk_grouped_path(const uint16_t* x, int T, int K, const uint8_t* codes, const uint16_t* scales,
+                                   int E, int N, int topk, const int32_t* expert_off, const int32_t* sorted_pairs,
+                                   float* gate_up, float* act, void* workspace, size_t workspace_bytes, int path,
+                                   void* stream) {
+  return gateup_fp8(x, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up, act, false, workspace,
+                    workspace_bytes, path, stream);
+}
+
+int moe_gateup_fp8blk_grouped_act_bf16(const uint16_t* x, int T, int K, const uint8_t* codes,
+                                       const uint16_t* scales, int E, int N, int topk, const int32_t* expert_off,
+                                       const int32_t* sorted_pairs, float* gate_up, uint16_t* act_bf16,
+                                       void* workspace, size_t workspace_bytes, int path, void* stream) {
+  return gateup_fp8(x, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up, act_bf16, true,
+                    workspace, workspace_bytes, path, stream);
 }
 
 int moe_gateup_fp8blk_grouped(const uint16_t* x, int T, int K, const uint8_t* codes, const uint16_t* scales, int E,
@@ -393,9 +429,14 @@ size_t moe_gateup_i8g_workspace_size(int T, int K) {
   return i8g_ws_total(T, K);
 }
 
-int moe_gateup_i8g_grouped(const uint16_t* x, int T, int K, const int8_t* codes, const uint16_t* scales, int E,
-                           int N, int topk, const int32_t* expert_off, const int32_t* sorted_pairs, float* gate_up,
-                           float* act, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// act: float32 [P, I], or bf16 [P, I] when act_bf16
+int gateup_i8g(const uint16_t* x, int T, int K, const int8_t* codes, const uint16_t* scales, int E, int N,
+               int topk, const int32_t* expert_off, const int32_t* sorted_pairs, float* gate_up, void* act,
+               bool act_bf16, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_common_moe(T, K, E, N, topk);
   if (rc != I8H_OK) return rc;
   if ((N % 2) != 0) return I8H_EINVAL;                  // gate and up halves
@@ -406,7 +447,7 @@ int moe_gateup_i8g_grouped(const uint16_t* x, int T, int K, const int8_t* codes,
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(expert_off, 4) ||
       !aligned(sorted_pairs, 4))
     return I8H_EINVAL;
-  if ((gate_up && !aligned(gate_up, 4)) || (act && !aligned(act, 4))) return I8H_EINVAL;
+  if ((gate_up && !aligned(gate_up, 4)) || (act && !aligned(act, act_bf16 ? 2 : 4))) return I8H_EINVAL;
   if (!workspace || workspace_bytes < i8g_ws_total(T, K) || !aligned(workspace, 256)) return I8H_EINVAL;
   if (!gate_up && !act) return I8H_OK;
   int8_t* qx = static_cast<int8_t*>(workspace);
@@ -414,8 +455,29 @@ int moe_gateup_i8g_grouped(const uint16_t* x, int T, int K, const int8_t* codes,
   hipStream_t st = as_stream(stream);
   if (i8h::launch_i8_act_quant(x, T, K, qx, sx, st) != hipSuccess) return I8H_EHIP;
   return from_hip(i8h::launch_gateup_i8g(qx, sx, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up,
-                                         act, st));
+                                         act, act_bf16, st));
 }
+
+}  // namespace
+
+extern "C" {
+
+int moe_gateup_i8g_grouped(const uint16_t* x, int T, int K, const int8_t* codes, const uint16_t* scales, int E,
+                           int N, int topk, const int32_t* expert_off, const int32_t* sorted_pairs, float* gate_up,
+                           float* act, void* workspace, size_t workspace_bytes, void* stream) {
+  return gateup_i8g(x, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up, act, false, workspace,
+                    workspace_bytes, stream);
+}
+
+int moe_gateup_i8g_grouped_act_bf16(const uint16_t* x, int T, int K, const int8_t* codes, const uint16_t* scales,
+                                    int E, int N, int topk, const int32_t* expert_off, const int32_t* sorted_pairs,
+                                    float* gate_up, uint16_t* act_bf16, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  return gateup_i8g(x, T, K, codes, scales, E, N, topk, expert_off, sorted_pairs, gate_up, act_bf16, true,
+                    workspace, workspace_bytes, stream);
+}
+
+
 
 // bf16 grouped down projection + weighted combine
 size_t moe_down_bf16_workspace_size(int T, int I, int H, int topk) {
@@ -427,7 +489,7 @@ int moe_down_bf16_combine(const float* act, int T, int I, const uint16_t* w_down
                           const int32_t* topk_ids, const float* topk_w, const int32_t* expert_off,
                           const int32_t* pair_pos, float* out, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  return down_combine(act, T, I, w_down, E, H, topk, topk_ids, topk_w, expert_off, pair_pos, out, workspace,
+  return down_combine(act, false, T, I, w_down, E, H, topk, topk_ids, topk_w, expert_off, pair_pos, out, workspace,
                       workspace_bytes, I8H_DOWN_AUTO, stream);
 }
 
@@ -435,8 +497,21 @@ int moe_down_bf16_combine_path(const float* act, int T, int I, const uint16_t* w
                                const int32_t* topk_ids, const float* topk_w, const int32_t* expert_off,
                                const int32_t* pair_pos, float* out, void* workspace, size_t workspace_bytes,
                                int path, void* stream) {
-  return down_combine(act, T, I, w_down, E, H, topk, topk_ids, topk_w, expert_off, pair_pos, out, workspace,
+  return down_combine(act, false, T, I, w_down, E, H, topk, topk_ids, topk_w, expert_off, pair_pos, out, workspace,
                       workspace_bytes, path, stream);
+}
+
+size_t moe_down_bf16_act_bf16_workspace_size(int T, int I, int H, int topk) {
+  if (T <= 0 || I <= 0 || H <= 0 || topk <= 0) return 0;
+  return DownWs(T, I, H, topk).y;
+}
+
+int moe_down_bf16_combine_act_bf16(const uint16_t* act_bf16, int T, int I, const uint16_t* w_down, int E, int H,
+                                   int topk, const int32_t* topk_ids, const float* topk_w,
+                                   const int32_t* expert_off, const int32_t* pair_pos, float* out,
+                                   void* workspace, size_t workspace_bytes, int path, void* stream) {
+  return down_combine(act_bf16, true, T, I, w_down, E, H, topk, topk_ids, topk_w, expert_off, pair_pos, out,
+                      workspace, workspace_bytes, path, stream);
 }
 
 // dense int8 linear with f16 group scales (the drafter's linears)

@@ -51,6 +51,13 @@ __device__ __forceinline__ float gelu_tanh(float v) {
   return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
 
+// One act value stored as float32, or as bf16 rounded to nearest even from that
+// float32 value (the rounding the bf16 down projection applies to its input).
+__device__ __forceinline__ void put_act(float* p, size_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void put_act(uint16_t* p, size_t i, float v) {
+  p[i] = __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
 __host__ __device__ constexpr inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 }  // namespace i8h

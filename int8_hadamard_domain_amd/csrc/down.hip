@@ -4,7 +4,8 @@
 // The int8 card's model table (row "Weights") keeps the experts' down
 // projections in bf16. W_down[e] is [H, I] row-major (H = the hidden size);
 // the float32 act rows of the gate_up epilogue are rounded to bf16 (nearest
-// even) for the product, which accumulates in float32 (products of two bf16
+// even) for the product, or come already rounded (the gate_up epilogue's bf16
+// form, AT = uint16_t), and it accumulates in float32 (products of two bf16
 // values are exact in float32; the few-pairs form adds them two at a time
 // with v_dot2_f32_bf16):
 //   y[r, h]   = sum_i W_down[e(r), h, i] * bf16(act[r, i])      (sorted row r)
@@ -16,7 +17,8 @@
 //     streams the 8 rows of one expert with 16-byte loads and dots them with
 //     the token's act row for that slot; the 8 x k partial dots meet in LDS
 //     and are merged in slot order. No intermediate y, one launch.
-//   * many pairs (verify, prefill): act -> bf16 once, a grouped bf16 MFMA GEMM
+//   * many pairs (verify, prefill): act -> bf16 once (nothing to do for bf16
+//     act), a grouped bf16 MFMA GEMM
 //     writes y in sorted order, then a combine kernel merges the k rows of
 //     each token. The GEMM is persistent: a workgroup per CU streams work
 //     items (expert, 256 output columns), each in passes of 256 sorted rows,
@@ -52,9 +54,9 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 constexpr int kDvThreads = 256;  // 8 half-waves
 
 // NQ: 16-byte pieces (8 bf16) per lane per row, I <= 256 * NQ
-template <int NQ>
+template <int NQ, typename AT>
 __global__ void __launch_bounds__(kDvThreads)
-k_down_gemv_combine(const float* __restrict__ act, int I, const uint16_t* __restrict__ w, int H, int k,
+k_down_gemv_combine(const AT* __restrict__ act, int I, const uint16_t* __restrict__ w, int H, int k,
                     const int32_t* __restrict__ ids, const float* __restrict__ tw,
                     const int32_t* __restrict__ pos, float* __restrict__ out) {
   __shared__ float part[kMaxTopk][kDvRows];
@@ -80,15 +82,22 @@ k_down_gemv_combine(const float* __restrict__ act, int I, const uint16_t* __rest
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int c = l + 32 * q;
-      f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
-      if (c < npc) {
-        lo = *reinterpret_cast<const f32x4*>(act + (size_t)r * I + 8 * c);
-        hi = *reinterpret_cast<const f32x4*>(act + (size_t)r * I + 8 * c + 4);
+      if constexpr (std::is_same_v<AT, float>) {
+        f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+        if (c < npc) {
+          lo = *reinterpret_cast<const f32x4*>(act + (size_t)r * I + 8 * c);
+          hi = *reinterpret_cast<const f32x4*>(act + (size_t)r * I + 8 * c + 4);
+        }
+        a[q][0] = pack_bf16x2(lo[0], lo[1]);
+        a[q][1] = pack_bf16x2(lo[2], lo[3]);
+        a[q][2] = pack_bf16x2(hi[0], hi[1]);
+        a[q][3] = pack_bf16x2(hi[2], hi[3]);
+      } else {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (c < npc) v = *reinterpret_cast<const u32x4*>(act + (size_t)r * I + 8 * c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[q][i] = v[i];
       }
-      a[q][0] = pack_bf16x2(lo[0], lo[1]);
-      a[q][1] = pack_bf16x2(lo[2], lo[3]);
-      a[q][2] = pack_bf16x2(hi[0], hi[1]);
-      a[q][3] = pack_bf16x2(hi[2], hi[3]);
     }
 #pragma unroll
     for (int row = 0; row < kDvRows; ++row) {
@@ -412,9 +421,9 @@ __global__ void k_down_combine(const float* __restrict__ y, int H, int k, const 
 
 }  // namespace
 
-hipError_t launch_down_gemv_combine(const float* act, int T, int I, const uint16_t* w, int H, int k,
-                                    const int32_t* ids, const float* tw, const int32_t* pos, float* out,
-                                    hipStream_t st) {
+template <typename AT>
+static hipError_t down_gemv(const AT* act, int T, int I, const uint16_t* w, int H, int k, const int32_t* ids,
+                            const float* tw, const int32_t* pos, float* out, hipStream_t st) {
   const dim3 grid(H / kDvRows, T);
   const int nq = cdiv(I, 256);
   switch (nq) {
@@ -427,16 +436,28 @@ hipError_t launch_down_gemv_combine(const float* act, int T, int I, const uint16
   return hipGetLastError();
 }
 
-hipError_t launch_down_gemm_combine(const float* act, int T, int I, const uint16_t* w, int E, int H, int k,
-                                    const float* tw, const int32_t* expert_off, const int32_t* pos,
+hipError_t launch_down_gemv_combine(const void* act, bool act_bf16, int T, int I, const uint16_t* w, int H, int k,
+                                    const int32_t* ids, const float* tw, const int32_t* pos, float* out,
+                                    hipStream_t st) {
+  if (act_bf16) return down_gemv(static_cast<const uint16_t*>(act), T, I, w, H, k, ids, tw, pos, out, st);
+  return down_gemv(static_cast<const float*>(act), T, I, w, H, k, ids, tw, pos, out, st);
+}
+
+hipError_t launch_down_gemm_combine(const void* act, bool act_bf16, int T, int I, const uint16_t* w, int E, int H,
+                                    int k, const float* tw, const int32_t* expert_off, const int32_t* pos,
                                     uint16_t* a16, float* y, float* out, hipStream_t st) {
-  const int64_t n8 = (int64_t)T * k * I / 8;
-  k_f32_to_bf16<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(act, a16, n8);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  hipError_t err;
+  const uint16_t* a = static_cast<const uint16_t*>(act);
+  if (!act_bf16) {
+    const int64_t n8 = (int64_t)T * k * I / 8;
+    k_f32_to_bf16<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(static_cast<const float*>(act), a16, n8);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    a = a16;
+  }
   const int ntiles = H / kDgCols;
   const int grid = min(cdiv(E, kDgXcds) * kDgXcds * ntiles, kDgBlocks);   // both multiples of 8
-  k_down_gemm<<<grid, kDgThreads, 0, st>>>(a16, I, w, E, H, expert_off, y, ntiles);
+  k_down_gemm<<<grid, kDgThreads, 0, st>>>(a, I, w, E, H, expert_off, y, ntiles);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   k_down_combine<<<dim3(cdiv(H / 4, 256), T), 256, 0, st>>>(y, H, k, tw, pos, out);

@@ -7,7 +7,8 @@
 // scale per block; activations quantized per token and 128 of K (float32
 // scale sx, E4M3 codes qx, handed over here as their exact bf16 values).
 //   gu[r, n] = sum_g (sw[e, n/128, g] * sx[t, g]) * sum_{kk in g} qw * qx
-// Both: act[r, i] = gelu_tanh(gu[r, i]) * gu[r, I + i].
+// Both: act[r, i] = gelu_tanh(gu[r, i]) * gu[r, I + i], stored as float32 or
+// (AT = uint16_t) as bf16 rounded to nearest even from the float32 value.
 //
 // Work unit = (expert e, 128 gate rows + the 128 matching up rows). Blocks
 // are mapped so that the units of one expert run on one XCD (the hardware
@@ -145,12 +146,12 @@ __device__ __forceinline__ void dma4s(uint32_t off, const void* base, uint32_t l
 __device__ __forceinline__ int a_pos(int row, int piece) { return piece ^ ((row >> 1) & 7); }
 __device__ __forceinline__ int b_pos(int row, int piece) { return piece ^ ((row >> 2) & 3); }
 
-template <WFmt F>
+template <WFmt F, typename AT>
 __global__ void __launch_bounds__(kGThreads)
 k_gateup_gemm(const uint16_t* __restrict__ xa, const float* __restrict__ sx, int K,
               const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int E, int N, int k,
               const int32_t* __restrict__ expert_off, const int32_t* __restrict__ sorted_pairs,
-              float* __restrict__ gu, float* __restrict__ act, int ntiles) {
+              float* __restrict__ gu, AT* __restrict__ act, int ntiles) {
   // unit: the units of expert e run on XCD e % 8, consecutive in dispatch order
   const int blk = blockIdx.x;
   const int slot = blk / kXcds;
@@ -354,7 +355,7 @@ k_gateup_gemm(const uint16_t* __restrict__ xa, const float* __restrict__ sx, int
               gu[r * N + i0 + col] = gv;
               gu[r * N + I + i0 + col] = uv;
             }
-            if (act) act[r * I + i0 + col] = gelu_tanh(gv) * uv;
+            if (act) put_act(act, r * I + i0 + col, gelu_tanh(gv) * uv);
           }
         }
       }
@@ -437,11 +438,12 @@ struct TallPass {
   f32x16 R[4][2];
 };
 
+template <typename AT>
 __global__ void __launch_bounds__(kTThreads)
 k_gateup_gemm_tall(const uint16_t* __restrict__ xa, int K, const uint8_t* __restrict__ codes,
                    const uint16_t* __restrict__ scales, int E, int N, int k,
                    const int32_t* __restrict__ expert_off, const int32_t* __restrict__ sorted_pairs,
-                   float* __restrict__ gu, float* __restrict__ act, int ntiles) {
+                   float* __restrict__ gu, AT* __restrict__ act, int ntiles) {
   const int blk = blockIdx.x;
   const int slot = blk / kXcds;
   const int e = (blk % kXcds) + kXcds * (slot / ntiles);
@@ -664,7 +666,7 @@ k_gateup_gemm_tall(const uint16_t* __restrict__ xa, int K, const uint8_t* __rest
               gu[r * N + i0 + col] = gv;
               gu[r * N + I + i0 + col] = uv;
             }
-            if (act) act[r * I + i0 + col] = gelu_tanh(gv) * uv;
+            if (act) put_act(act, r * I + i0 + col, gelu_tanh(gv) * uv);
           }
         }
       }
@@ -676,34 +678,53 @@ static int gemm_grid(int E, int ntiles) { return cdiv(E, kXcds) * kXcds * ntiles
 
 hipError_t launch_gateup_i8h_gemm_tall(const uint16_t* xrot, int T, int K, const int8_t* codes,
                                        const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
-                                       const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st) {
+                                       const int32_t* sorted_pairs, float* gu, void* act, bool act_bf16,
+                                       hipStream_t st) {
   (void)T;
   int ntiles = cdiv(N / 2, kTGate);
-  k_gateup_gemm_tall<<<gemm_grid(E, ntiles), kTThreads, 0, st>>>(
-      xrot, K, reinterpret_cast<const uint8_t*>(codes), scales, E, N, k, expert_off, sorted_pairs, gu, act,
-      ntiles);
+  const uint8_t* q = reinterpret_cast<const uint8_t*>(codes);
+  if (act_bf16)
+    k_gateup_gemm_tall<<<gemm_grid(E, ntiles), kTThreads, 0, st>>>(xrot, K, q, scales, E, N, k, expert_off,
+                                                                   sorted_pairs, gu,
+                                                                   static_cast<uint16_t*>(act), ntiles);
+  else
+    k_gateup_gemm_tall<<<gemm_grid(E, ntiles), kTThreads, 0, st>>>(xrot, K, q, scales, E, N, k, expert_off,
+                                                                   sorted_pairs, gu, static_cast<float*>(act),
+                                                                   ntiles);
+  return hipGetLastError();
+}
+
+template <WFmt F>
+static hipError_t launch_gemm(const uint16_t* xa, const float* sx, int K, const uint8_t* codes,
+                              const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
+                              const int32_t* sorted_pairs, float* gu, void* act, bool act_bf16, hipStream_t st) {
+  const int ntiles = cdiv(N / 2, kGateRows);
+  if (act_bf16)
+    k_gateup_gemm<F><<<gemm_grid(E, ntiles), kGThreads, 0, st>>>(xa, sx, K, codes, scales, E, N, k, expert_off,
+                                                                 sorted_pairs, gu, static_cast<uint16_t*>(act),
+                                                                 ntiles);
+  else
+    k_gateup_gemm<F><<<gemm_grid(E, ntiles), kGThreads, 0, st>>>(xa, sx, K, codes, scales, E, N, k, expert_off,
+                                                                 sorted_pairs, gu, static_cast<float*>(act),
+                                                                 ntiles);
   return hipGetLastError();
 }
 
 hipError_t launch_gateup_i8h_gemm(const uint16_t* xrot, int T, int K, const int8_t* codes,
                                   const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
-                                  const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st) {
+                                  const int32_t* sorted_pairs, float* gu, void* act, bool act_bf16,
+                                  hipStream_t st) {
   (void)T;
-  int ntiles = cdiv(N / 2, kGateRows);
-  k_gateup_gemm<WFmt::I8><<<gemm_grid(E, ntiles), kGThreads, 0, st>>>(
-      xrot, nullptr, K, reinterpret_cast<const uint8_t*>(codes), scales, E, N, k, expert_off, sorted_pairs, gu,
-      act, ntiles);
-  return hipGetLastError();
+  return launch_gemm<WFmt::I8>(xrot, nullptr, K, reinterpret_cast<const uint8_t*>(codes), scales, E, N, k,
+                               expert_off, sorted_pairs, gu, act, act_bf16, st);
 }
 
 hipError_t launch_gateup_fp8(const uint16_t* xq, const float* sx, int T, int K, const uint8_t* codes,
                              const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
-                             const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st) {
+                             const int32_t* sorted_pairs, float* gu, void* act, bool act_bf16, hipStream_t st) {
   (void)T;
-  int ntiles = cdiv(N / 2, kGateRows);
-  k_gateup_gemm<WFmt::E4M3><<<gemm_grid(E, ntiles), kGThreads, 0, st>>>(
-      xq, sx, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu, act, ntiles);
-  return hipGetLastError();
+  return launch_gemm<WFmt::E4M3>(xq, sx, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu, act, act_bf16,
+                                 st);
 }
 
 }  // namespace i8h

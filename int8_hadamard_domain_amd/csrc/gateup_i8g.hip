@@ -6,6 +6,8 @@
 //   sx[t, g] = amax_g / 127 (IEEE single division), qx = rne(x / sx) clamped to +-127
 //   gu[r, n] = sum_g sw[e, n, g] * sx[t, g] * sum_{kk in g} qw[e, n, kk] * qx[t, kk]
 //   act[r, i] = gelu_tanh(gu[r, i]) * gu[r, I + i]
+// (act stored as float32, or with AT = uint16_t as bf16 rounded to nearest
+// even from the float32 value)
 //
 // Both operands stay int8 all the way into v_mfma_i32_32x32x32_i8: the group
 // sums are exact int32 (|sum| <= 128 * 127 * 127 < 2^21), and each is folded
@@ -100,10 +102,11 @@ constexpr int kVmcnt0 = (0x7 << 4) | (0xF << 8);
 
 __device__ __forceinline__ int g_pos(int row, int piece) { return piece ^ ((row >> 1) & 7); }
 
+template <typename AT>
 __global__ void __launch_bounds__(kIThreads)
 k_gateup_i8g(const int8_t* __restrict__ qx, const float* __restrict__ sx, int K, const int8_t* __restrict__ codes,
              const uint16_t* __restrict__ scales, int E, int N, int k, const int32_t* __restrict__ expert_off,
-             const int32_t* __restrict__ sorted_pairs, float* __restrict__ gu, float* __restrict__ act, int ntiles) {
+             const int32_t* __restrict__ sorted_pairs, float* __restrict__ gu, AT* __restrict__ act, int ntiles) {
   // the units of expert e run on XCD e % 8, consecutive in dispatch order
   const int blk = blockIdx.x;
   const int slot = blk / kIXcds;
@@ -252,7 +255,7 @@ k_gateup_i8g(const int8_t* __restrict__ qx, const float* __restrict__ sx, int K,
     if (live) {
       // uniform bases and 32-bit lane offsets, opaque so the compiler does
       // not hoist the store addresses of every pass out of the pass loop
-      float* act_b = act ? act + (size_t)(r0 + mb) * I : nullptr;
+      AT* act_b = act ? act + (size_t)(r0 + mb) * I : nullptr;
       float* gu_b = gu ? gu + (size_t)(r0 + mb) * N : nullptr;
 #pragma unroll
       for (int a = 0; a < kIMt; ++a) {
@@ -269,7 +272,7 @@ k_gateup_i8g(const int8_t* __restrict__ qx, const float* __restrict__ sx, int K,
               gu_b[go + (uint32_t)(dm * N)] = gv;
               gu_b[go + (uint32_t)(dm * N + I)] = uv;
             }
-            if (act_b) act_b[ao + (uint32_t)(dm * I)] = gelu_tanh(gv) * uv;
+            if (act_b) put_act(act_b, ao + (uint32_t)(dm * I), gelu_tanh(gv) * uv);
           }
         }
       }
@@ -330,12 +333,16 @@ hipError_t launch_i8_act_quant(const uint16_t* x, int T, int K, int8_t* qx, floa
 
 hipError_t launch_gateup_i8g(const int8_t* qx, const float* sx, int T, int K, const int8_t* codes,
                              const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
-                             const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st) {
+                             const int32_t* sorted_pairs, float* gu, void* act, bool act_bf16, hipStream_t st) {
   (void)T;
   const int ntiles = cdiv(N / 2, kICols);
   const int grid = cdiv(E, kIXcds) * kIXcds * ntiles;
-  k_gateup_i8g<<<grid, kIThreads, 0, st>>>(qx, sx, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu, act,
-                                           ntiles);
+  if (act_bf16)
+    k_gateup_i8g<<<grid, kIThreads, 0, st>>>(qx, sx, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu,
+                                             static_cast<uint16_t*>(act), ntiles);
+  else
+    k_gateup_i8g<<<grid, kIThreads, 0, st>>>(qx, sx, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu,
+                                             static_cast<float*>(act), ntiles);
   return hipGetLastError();
 }
 

@@ -5,6 +5,8 @@
 // row r of expert e and token t:
 //   gu[r, n] = sum_g s[e, n, g] * sum_{kk in g} q[e, n, kk] * x_rot[t, kk]
 //   act[r, i] = gelu_tanh(gu[r, i]) * gu[r, I + i]
+// (act stored as float32, or by the grouped GEMV with AT = uint16_t as bf16
+// rounded to nearest even from the float32 value)
 //
 // Work split: grid y = slot of a non-empty expert, grid x = groups of row
 // pairs (i, I + i). Each wave owns RPW row pairs and issues all of their code
@@ -220,9 +222,9 @@ __device__ __forceinline__ void prep_x(const XRow<NCH>& X, float (&xv)[NCH][16],
 // activation values xv), stored at sorted row r. PIN_SCALES keeps the scale
 // conversions inside the caller's row loop (where the activation row is
 // prepared before the codes arrive, they must not wait for the scale loads).
-template <int NCH, int RPW, bool PIN_SCALES>
+template <int NCH, int RPW, bool PIN_SCALES, typename AT>
 __device__ __forceinline__ void gemv_row(const WaveRows<NCH, RPW>& R, const float (&xv)[NCH][16], int K, int N,
-                                         int i0, size_t r, float* __restrict__ gu, float* __restrict__ act,
+                                         int i0, size_t r, float* __restrict__ gu, AT* __restrict__ act,
                                          int lane) {
   const int I = N / 2, G = K / kGroup;
   float v[2 * RPW];
@@ -297,16 +299,16 @@ __device__ __forceinline__ void gemv_row(const WaveRows<NCH, RPW>& R, const floa
       gu[r * N + i0 + j] = g;
       gu[r * N + I + i0 + j] = u;
     }
-    if (act) act[r * I + i0 + j] = gelu_tanh(g) * u;
+    if (act) put_act(act, r * I + i0 + j, gelu_tanh(g) * u);
   }
 }
 
-template <int NCH, int RPW, bool ROT>
+template <int NCH, int RPW, bool ROT, typename AT>
 __global__ void __launch_bounds__(kGemvThreads)
 k_gateup_i8h_gemv(const uint16_t* __restrict__ xin, int K, const int8_t* __restrict__ codes,
                   const uint16_t* __restrict__ scales, int E, int N, int k,
                   const int32_t* __restrict__ expert_off, const int32_t* __restrict__ sorted_pairs,
-                  float* __restrict__ gu, float* __restrict__ act) {
+                  float* __restrict__ gu, AT* __restrict__ act) {
   static_assert(RPW == 2 || RPW == 4, "2*RPW values per lane are folded over bits 5..");
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: row bases in SGPRs
@@ -602,10 +604,10 @@ k_route_gateup_decode(const float* __restrict__ logits, const uint16_t* __restri
   }
 }
 
-template <bool ROT>
+template <bool ROT, typename AT>
 static hipError_t launch_gemv(const uint16_t* x, int T, int K, const int8_t* codes, const uint16_t* scales, int E,
                               int N, int k, const int32_t* expert_off, const int32_t* sorted_pairs, float* gu,
-                              float* act, hipStream_t st) {
+                              AT* act, hipStream_t st) {
   int P = T * k;
   int slots = P < E ? P : E;  // at most this many experts can be non-empty
   int I = N / 2;
@@ -628,8 +630,13 @@ static hipError_t launch_gemv(const uint16_t* x, int T, int K, const int8_t* cod
 
 hipError_t launch_gateup_i8h_gemv(const uint16_t* xrot, int T, int K, const int8_t* codes,
                                   const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
-                                  const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st) {
-  return launch_gemv<false>(xrot, T, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu, act, st);
+                                  const int32_t* sorted_pairs, float* gu, void* act, bool act_bf16,
+                                  hipStream_t st) {
+  if (act_bf16)
+    return launch_gemv<false>(xrot, T, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu,
+                              static_cast<uint16_t*>(act), st);
+  return launch_gemv<false>(xrot, T, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu,
+                            static_cast<float*>(act), st);
 }
 
 hipError_t launch_gateup_i8h_gemv_rot(const uint16_t* x, int T, int K, const int8_t* codes,

@@ -8,7 +8,8 @@
 // scale per block, activations quantized per token and 128 of K (float32
 // factor sx, E4M3 codes handed over as their exact bf16 values).
 //   gu[r, n] = sum_g (sw[e, n/128, g] * sx[t, g]) * sum_{kk in g} qw * qx
-// Both: act[r, i] = gelu_tanh(gu[r, i]) * gu[r, I + i].
+// Both: act[r, i] = gelu_tanh(gu[r, i]) * gu[r, I + i], stored as float32 or
+// (AT = uint16_t) as bf16 rounded to nearest even from the float32 value.
 //
 // With a handful of pairs per expert the step is a stream of the touched
 // experts' codes, and what bounds it is how many bytes each CU keeps in
@@ -134,12 +135,12 @@ __device__ __forceinline__ bf16x8 s_decode(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x8, p);
 }
 
-template <SFmt F, bool KS>
+template <SFmt F, bool KS, typename AT>
 __device__ __forceinline__ void skinny_body(const uint16_t* __restrict__ xa, const float* __restrict__ sx, int K,
                                             const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
                                             int E, int N, int k, const int32_t* __restrict__ expert_off,
                                             const int32_t* __restrict__ sorted_pairs, float* __restrict__ gu,
-                                            float* __restrict__ act, int ntiles) {
+                                            AT* __restrict__ act, int ntiles) {
   // the units of expert e run on XCD e % 8, consecutive in dispatch order
   const int blk = blockIdx.x;
   const int slot = blk / kSXcds;
@@ -355,7 +356,7 @@ __device__ __forceinline__ void skinny_body(const uint16_t* __restrict__ xa, con
     if (busy && !(ksplit && kh == 1)) {
       // uniform bases and 32-bit lane offsets, opaque so the compiler does
       // not hoist the store addresses of every pass out of the pass loop
-      float* act_b = act ? act + (size_t)(r0 + mb) * I : nullptr;
+      AT* act_b = act ? act + (size_t)(r0 + mb) * I : nullptr;
       float* gu_b = gu ? gu + (size_t)(r0 + mb) * N : nullptr;
       uint32_t go = (uint32_t)((mt + 4 * half) * N + i0 + col), ao = (uint32_t)((mt + 4 * half) * I + i0 + col);
       asm volatile("" : "+v"(go), "+v"(ao));
@@ -368,7 +369,7 @@ __device__ __forceinline__ void skinny_body(const uint16_t* __restrict__ xa, con
             gu_b[go + (uint32_t)(dm * N)] = gv;
             gu_b[go + (uint32_t)(dm * N + I)] = uv;
           }
-          if (act_b) act_b[ao + (uint32_t)(dm * I)] = gelu_tanh(gv) * uv;
+          if (act_b) put_act(act_b, ao + (uint32_t)(dm * I), gelu_tanh(gv) * uv);
         }
       }
     }
@@ -384,22 +385,24 @@ __device__ __forceinline__ bool skinny_split(int E, const int32_t* __restrict__ 
   return m_e <= 32;
 }
 
+template <typename AT>
 __global__ void __launch_bounds__(kSThreads, 3)
 k_gateup_i8h_skinny(const uint16_t* __restrict__ xa, int K, const uint8_t* __restrict__ codes,
                     const uint16_t* __restrict__ scales, int E, int N, int k,
                     const int32_t* __restrict__ expert_off, const int32_t* __restrict__ sorted_pairs,
-                    float* __restrict__ gu, float* __restrict__ act, int ntiles) {
+                    float* __restrict__ gu, AT* __restrict__ act, int ntiles) {
   if (skinny_split(E, expert_off, ntiles))
     skinny_body<SFmt::I8, true>(xa, nullptr, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu, act, ntiles);
   else
     skinny_body<SFmt::I8, false>(xa, nullptr, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu, act, ntiles);
 }
 
+template <typename AT>
 __global__ void __launch_bounds__(kSThreads, 3)
 k_gateup_fp8_skinny(const uint16_t* __restrict__ xq, const float* __restrict__ sx, int K,
                     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int E, int N, int k,
                     const int32_t* __restrict__ expert_off, const int32_t* __restrict__ sorted_pairs,
-                    float* __restrict__ gu, float* __restrict__ act, int ntiles) {
+                    float* __restrict__ gu, AT* __restrict__ act, int ntiles) {
   if (skinny_split(E, expert_off, ntiles))
     skinny_body<SFmt::E4M3, true>(xq, sx, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu, act, ntiles);
   else
@@ -410,23 +413,34 @@ k_gateup_fp8_skinny(const uint16_t* __restrict__ xq, const float* __restrict__ s
 
 hipError_t launch_gateup_i8h_skinny(const uint16_t* xrot, int T, int K, const int8_t* codes,
                                     const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
-                                    const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st) {
+                                    const int32_t* sorted_pairs, float* gu, void* act, bool act_bf16,
+                                    hipStream_t st) {
   (void)T;
   const int ntiles = cdiv(N / 2, kSGate);
   const int grid = cdiv(E, kSXcds) * kSXcds * ntiles;
-  k_gateup_i8h_skinny<<<grid, kSThreads, 0, st>>>(xrot, K, reinterpret_cast<const uint8_t*>(codes), scales, E, N,
-                                                  k, expert_off, sorted_pairs, gu, act, ntiles);
+  const uint8_t* q = reinterpret_cast<const uint8_t*>(codes);
+  if (act_bf16)
+    k_gateup_i8h_skinny<<<grid, kSThreads, 0, st>>>(xrot, K, q, scales, E, N, k, expert_off, sorted_pairs, gu,
+                                                    static_cast<uint16_t*>(act), ntiles);
+  else
+    k_gateup_i8h_skinny<<<grid, kSThreads, 0, st>>>(xrot, K, q, scales, E, N, k, expert_off, sorted_pairs, gu,
+                                                    static_cast<float*>(act), ntiles);
   return hipGetLastError();
 }
 
 hipError_t launch_gateup_fp8_skinny(const uint16_t* xq, const float* sx, int T, int K, const uint8_t* codes,
                                     const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
-                                    const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st) {
+                                    const int32_t* sorted_pairs, float* gu, void* act, bool act_bf16,
+                                    hipStream_t st) {
   (void)T;
   const int ntiles = cdiv(N / 2, kSGate);
   const int grid = cdiv(E, kSXcds) * kSXcds * ntiles;
-  k_gateup_fp8_skinny<<<grid, kSThreads, 0, st>>>(xq, sx, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu,
-                                                  act, ntiles);
+  if (act_bf16)
+    k_gateup_fp8_skinny<<<grid, kSThreads, 0, st>>>(xq, sx, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu,
+                                                    static_cast<uint16_t*>(act), ntiles);
+  else
+    k_gateup_fp8_skinny<<<grid, kSThreads, 0, st>>>(xq, sx, K, codes, scales, E, N, k, expert_off, sorted_pairs, gu,
+                                                    static_cast<float*>(act), ntiles);
   return hipGetLastError();
 }
 

@@ -26,30 +26,38 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
 hipError_t launch_fwht128(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy, int T, int K,
                           hipStream_t st);
 
+// gate_up launchers: act is float32 [P, I], or bf16 [P, I] when act_bf16 (each
+// value rounded to nearest even from the float32 one)
 hipError_t launch_gateup_i8h_gemv(const uint16_t* xrot, int T, int K, const int8_t* codes,
                                   const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
-                                  const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st);
+                                  const int32_t* sorted_pairs, float* gu, void* act, bool act_bf16,
+                                  hipStream_t st);
 hipError_t launch_gateup_i8h_gemm(const uint16_t* xrot, int T, int K, const int8_t* codes,
                                   const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
-                                  const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st);
+                                  const int32_t* sorted_pairs, float* gu, void* act, bool act_bf16,
+                                  hipStream_t st);
 
 hipError_t launch_gateup_i8h_gemm_tall(const uint16_t* xrot, int T, int K, const int8_t* codes,
                                        const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
-                                       const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st);
+                                       const int32_t* sorted_pairs, float* gu, void* act, bool act_bf16,
+                                       hipStream_t st);
 
 hipError_t launch_gateup_i8h_skinny(const uint16_t* xrot, int T, int K, const int8_t* codes,
                                     const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
-                                    const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st);
+                                    const int32_t* sorted_pairs, float* gu, void* act, bool act_bf16,
+                                    hipStream_t st);
 
 hipError_t launch_gateup_fp8_skinny(const uint16_t* xq, const float* sx, int T, int K, const uint8_t* codes,
                                     const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
-                                    const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st);
+                                    const int32_t* sorted_pairs, float* gu, void* act, bool act_bf16,
+                                    hipStream_t st);
 
 hipError_t launch_i8_act_quant(const uint16_t* x, int T, int K, int8_t* qx, float* sx, hipStream_t st);
 
 hipError_t launch_gateup_i8g(const int8_t* qx, const float* sx, int T, int K, const int8_t* codes,
                              const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
-                             const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st);
+                             const int32_t* sorted_pairs, float* gu, void* act, bool act_bf16,
+                             hipStream_t st);
 
 hipError_t launch_gateup_i8h_gemv_rot(const uint16_t* x, int T, int K, const int8_t* codes,
                                       const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
@@ -64,14 +72,16 @@ hipError_t launch_fp8_act_quant(const uint16_t* x, int T, int K, uint8_t* qx, fl
                                 hipStream_t st);
 hipError_t launch_gateup_fp8(const uint16_t* xq, const float* sx, int T, int K, const uint8_t* codes,
                              const uint16_t* scales, int E, int N, int k, const int32_t* expert_off,
-                             const int32_t* sorted_pairs, float* gu, float* act, hipStream_t st);
+                             const int32_t* sorted_pairs, float* gu, void* act, bool act_bf16,
+                             hipStream_t st);
 
-// bf16 grouped down projection + weighted combine (down.hip)
-hipError_t launch_down_gemv_combine(const float* act, int T, int I, const uint16_t* w, int H, int k,
+// bf16 grouped down projection + weighted combine (down.hip); act is float32
+// [P, I], or bf16 [P, I] when act_bf16 (then a16 is not used)
+hipError_t launch_down_gemv_combine(const void* act, bool act_bf16, int T, int I, const uint16_t* w, int H, int k,
                                     const int32_t* ids, const float* tw, const int32_t* pos, float* out,
                                     hipStream_t st);
-hipError_t launch_down_gemm_combine(const float* act, int T, int I, const uint16_t* w, int E, int H, int k,
-                                    const float* tw, const int32_t* expert_off, const int32_t* pos,
+hipError_t launch_down_gemm_combine(const void* act, bool act_bf16, int T, int I, const uint16_t* w, int E, int H,
+                                    int k, const float* tw, const int32_t* expert_off, const int32_t* pos,
                                     uint16_t* a16, float* y, float* out, hipStream_t st);
 
 // dense int8 linear with f16 group scales (linear.hip)

@@ -33,7 +33,7 @@ def L():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 27, names
     for n in names:
         assert hasattr(L, n), n
 
@@ -240,6 +240,49 @@ def test_down_validation(L):
     assert down(L, T=100, ws=ctypes.c_void_p(0x10010)) == EINVAL   # not 256-B aligned
     assert down(L, I=2048, H=520, T=100) == EUNSUP    # neither form applies
     assert L.moe_down_bf16_combine(None, 4, 256, A, 8, 512, 2, A, A, A, A, A, A, 1 << 30, None) == EINVAL
+
+
+def test_act_bf16_entries_validation(L):
+    # the bf16 act forms: act 2-B aligned for the gate_up calls, 16-B for the down call, whose GEMM form
+    # needs a workspace for y only; the other checks as in the float32 forms
+    B1 = ctypes.c_void_p(0x10001)    # misaligned even for bf16
+    g = lambda act=A, gu=A, path=0, N=256, T=4, K=256: L.moe_gateup_i8h_grouped_act_bf16(
+        A, T, K, A, A, 8, N, 2, A, A, gu, act, path, None)
+    assert g(K=100) == EINVAL
+    assert g(N=97) == EINVAL
+    assert g(N=96) == EUNSUP
+    assert g(act=B1) == EINVAL
+    assert g(gu=ODD) == EINVAL
+    assert g(path=7) == EINVAL
+    assert g(T=0) == OK
+    assert g(gu=None, act=None) == OK
+    assert g(K=8192, path=1) == EUNSUP
+    f = L.moe_gateup_fp8blk_grouped_act_bf16
+    assert f(A, 4, 256, A, A, 8, 256, 2, A, A, A, B1, A, 1 << 20, 0, None) == EINVAL
+    assert f(A, 4, 256, A, A, 8, 192, 2, A, A, A, A, A, 1 << 20, 0, None) == EINVAL    # N % 128
+    assert f(A, 4, 256, A, A, 8, 256, 2, A, A, A, A, A, 1 << 20, 1, None) == EUNSUP    # GEMV: no E4M3 form
+    assert f(A, 4, 256, A, A, 8, 256, 2, A, A, A, A, None, 0, 0, None) == EINVAL       # no workspace
+    assert f(A, 0, 256, A, A, 8, 256, 2, A, A, A, A, None, 0, 0, None) == OK
+    w = L.moe_gateup_i8g_grouped_act_bf16
+    assert w(A, 4, 256, A, A, 8, 256, 2, A, A, A, B1, A, 1 << 20, None) == EINVAL
+    assert w(A, 4, 256, A, A, 8, 224, 2, A, A, A, A, A, 1 << 20, None) == EUNSUP
+    assert w(A, 4, 256, A, A, 8, 256, 2, A, A, A, A, None, 0, None) == EINVAL        # no workspace
+    assert w(A, 0, 256, A, A, 8, 256, 2, A, A, A, A, None, 0, None) == OK
+    # y only, rounded to 256 B
+    assert L.moe_down_bf16_act_bf16_workspace_size(2048, 768, 2048, 8) == 16384 * 2048 * 4
+    assert L.moe_down_bf16_act_bf16_workspace_size(1, 8, 8, 1) == 256
+    assert L.moe_down_bf16_act_bf16_workspace_size(0, 768, 2048, 8) == 0
+    need = L.moe_down_bf16_act_bf16_workspace_size(100, 256, 512, 2)
+    d = lambda act=A, T=100, I=256, H=512, ws=A, wsb=need, path=0: L.moe_down_bf16_combine_act_bf16(
+        act, T, I, A, 8, H, 2, A, A, A, A, A, ws, wsb, path, None)
+    assert d(I=100) == EINVAL
+    assert d(act=ctypes.c_void_p(0x10008)) == EINVAL          # 16-B alignment
+    assert d(act=None) == EINVAL
+    assert d(path=5) == EINVAL
+    assert d(T=0) == OK
+    assert d(ws=None) == EINVAL                               # AUTO takes the GEMM form: workspace needed
+    assert d(wsb=need - 1) == EINVAL                          # too small
+    assert d(I=2048, path=1) == EUNSUP
 
 
 def test_linear_validation(L):

@@ -76,6 +76,12 @@ def test_gateup_inputs_and_outputs(inp):
                                                act=torch.empty((T * k, N), device="cuda")))
     _raises(lambda: i8h.moe_gateup_i8h_grouped(x, codes, scales, k, off, sp,
                                                gate_up=torch.empty((T * k, N), dtype=torch.float64, device="cuda")))
+    # act: float32 or bfloat16 only, of shape [T*k, N/2] in either
+    _raises(lambda: i8h.moe_gateup_i8h_grouped(x, codes, scales, k, off, sp,
+                                               act=torch.empty((T * k, N // 2), dtype=torch.float64, device="cuda")))
+    _raises(lambda: i8h.moe_gateup_i8h_grouped(x, codes, scales, k, off, sp,
+                                               act=torch.empty((T * k, N), dtype=torch.bfloat16, device="cuda")))
+    _raises(lambda: i8h.moe_gateup_i8h_grouped(x, codes, scales, k, off, sp, act_dtype=torch.float16))
     _raises(lambda: i8h.moe_gateup_i8h_grouped(x, codes, scales, k, off[:-1].contiguous(), sp))
     _raises(lambda: i8h.moe_gateup_i8h_grouped(x, codes, scales, k + 1, off, sp))
     _raises(lambda: i8h.moe_gateup_i8h_grouped(x, codes, scales[:, :, :1].contiguous(), k, off, sp))
@@ -100,6 +106,10 @@ def test_down_and_linear(inp):
     _raises(lambda: i8h.moe_down_bf16_combine(act[:-1].contiguous(), w, r))
     _raises(lambda: i8h.moe_down_bf16_combine(act, w, r, out=torch.empty((T, H + 8), device="cuda")))
     _raises(lambda: i8h.moe_down_bf16_combine(act, w, r, path="gemm",
+                                              workspace=torch.empty((16,), dtype=torch.uint8, device="cuda")))
+    _raises(lambda: i8h.moe_down_bf16_combine(act.half(), w, r))
+    _raises(lambda: i8h.moe_down_bf16_combine(act.to(torch.bfloat16)[:-1].contiguous(), w, r))
+    _raises(lambda: i8h.moe_down_bf16_combine(act.to(torch.bfloat16), w, r, path="gemm",
                                               workspace=torch.empty((16,), dtype=torch.uint8, device="cuda")))
     bad = dict(r)
     bad["pair_pos"] = r["pair_pos"][:-1].contiguous()
