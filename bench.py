@@ -25,10 +25,13 @@ kernel alone, and the CPU oracle timed on a bounded sample of the same steps
 (one thread, then every thread; the CPU model is recorded). The decode step
 is the headline; the verify (T = 128) and prefill (T = 2048) steps are
 measured in the same run and reported under "rows", each with its own
-roofline (HBM, and the bf16 MFMA fraction). Every timed region runs at least
---steps steps and at least --min-ms of graph replays; the steps actually run
-are reported. A plain HBM read probe (libi8h_probe.so) runs first, and every
-roofline is also given as a fraction of what it reaches on the same GPU.
+roofline (HBM, and the bf16 MFMA fraction). Each line (the headline and
+every row) runs exactly --warmup untimed steps, then times exactly --steps
+steps between device synchronisations: whole graphs of the step cycle, then
+a graph of the remaining steps. The kernel-alone timings behind the
+rooflines replay graphs for at least --min-ms. A plain HBM read probe
+(libi8h_probe.so) runs first, and every roofline is also given as a fraction
+of what it reaches on the same GPU.
 """
 
 import argparse
@@ -50,11 +53,10 @@ METRIC = "weight GB/s and tokens/s, MoE gate_up at M=1/128/2048; % HBM / MFMA pe
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=512,
-                    help="least number of timed steps; more are run until the timed region reaches --min-ms")
-    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--steps", type=int, default=512, help="timed steps of each line (exactly)")
+    ap.add_argument("--warmup", type=int, default=64, help="untimed steps before them (exactly)")
     ap.add_argument("--min-ms", type=float, default=20.0,
-                    help="least length of each timed region (graph replays), whatever --steps says")
+                    help="least length of each kernel-alone timing (the rooflines' graph replays)")
     ap.add_argument("--workload", default="decode", choices=["decode", "verify", "prefill", "fp8", "w8a8"])
     ap.add_argument("--rows", default="auto",
                     help="comma list of further workloads measured in the same run and reported under 'rows' "
@@ -108,30 +110,34 @@ def capture_graph(fn, S, dev):
     return g
 
 
-def timed_replays(g, S, args, dev):
-    """Warm up with at least args.warmup steps (whole graphs, at least one),
-    then time at least args.steps steps and at least args.min_ms of replays,
-    bracketed by device synchronisations. Returns (steps, warmup steps, wall
-    seconds, per-step ms from HIP events on the replay stream)."""
+def timed_replays(g, S, args, dev, step):
+    """Exactly args.warmup untimed steps, then exactly args.steps timed steps,
+    bracketed by device synchronisations: whole replays of g (the cycle of S
+    steps), then a graph of the remaining steps (steps 0 .. r - 1 of the
+    cycle, captured beforehand from step). Returns (steps, warmup steps, wall
+    seconds of the timed region, per-step ms from HIP events on the replay
+    stream)."""
     import torch
-    warm_reps = max(1, -(-args.warmup // S))
-    t0 = time.perf_counter()
-    for _ in range(warm_reps):
+    K, W = max(1, args.steps), max(0, args.warmup)
+    tail_k = capture_graph(step, K % S, dev) if K % S else None
+    tail_w = capture_graph(step, W % S, dev) if W % S else None
+    for _ in range(W // S):
         g.replay()
-    torch.cuda.synchronize(dev)
-    per_rep = (time.perf_counter() - t0) / warm_reps
-    reps = max(1, -(-args.steps // S), int(np.ceil(1.15 * args.min_ms * 1e-3 / max(per_rep, 1e-7))))
+    if tail_w is not None:
+        tail_w.replay()
     st = torch.cuda.current_stream(dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     ev0.record(st)
-    for _ in range(reps):
+    for _ in range(K // S):
         g.replay()
+    if tail_k is not None:
+        tail_k.replay()
     ev1.record(st)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
-    return reps * S, warm_reps * S, wall, ev0.elapsed_time(ev1) / (reps * S)
+    return K, W, wall, ev0.elapsed_time(ev1) / K
 
 
 def main():
@@ -311,7 +317,7 @@ def measure_gate_up(args, name, dev, probe, keep_inputs):
     bytes_per_expert = L.N * L.K + (L.N // 128) * L.G * 2 if fp8 else L.N * L.K + L.N * L.G * 2
     weight_bytes = np.array(touched, dtype=np.float64) * bytes_per_expert   # per step in the graph
 
-    steps, warm, wall, step_ms_ev = timed_replays(g_step, S, args, dev)
+    steps, warm, wall, step_ms_ev = timed_replays(g_step, S, args, dev, step)
     ms_per_step = wall / steps * 1e3
     value = weight_bytes.mean() * steps / wall / 1e9
     tokens_per_s = L.T * steps / wall
@@ -563,7 +569,7 @@ def bench_down(args, L, dev):
     setup_s = time.perf_counter() - t_setup
     wbytes = np.array(touched, dtype=np.float64) * H * I * 2
 
-    steps, warm, wall, step_ms_ev = timed_replays(g, S, args, dev)
+    steps, warm, wall, step_ms_ev = timed_replays(g, S, args, dev, step)
     call_us = step_ms_ev * 1e3
     value = wbytes.mean() * steps / wall / 1e9
     # algorithmic bytes per call: touched W_down, act read once, out written, routing lists
@@ -657,7 +663,7 @@ def bench_linear(args, dev):
 
     g = capture_graph(step, S, dev)
     setup_s = time.perf_counter() - t_setup
-    steps, warm, wall, step_ms_ev = timed_replays(g, S, args, dev)
+    steps, warm, wall, step_ms_ev = timed_replays(g, S, args, dev, step)
     call_us = step_ms_ev * 1e3
     alg = wbytes + T * K * 2 + T * N * 4
     achieved = alg / (call_us * 1e-6) / 1e9
