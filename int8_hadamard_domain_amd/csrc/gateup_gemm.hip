@@ -35,7 +35,8 @@
 // into the float32 result with the group's scale (main += tmp * s); scaling
 // the codes first would round each weight to bf16. Codes become bf16
 // exactly: int8 by sign-extended byte converts (|q| <= 127 fits bf16's 8
-// significand bits), E4M3 by v_cvt_pk_f32_fp8 (3 significand bits).
+// significand bits), E4M3 two codes an instruction by the scaled pair
+// conversion v_cvt_scalef32_pk_bf16_fp8 with scale 1 (3 significand bits).
 //
 // MFMA operands (32x32x16 bf16): lane l feeds 8 values of row (A) or column
 // (B) l % 32 for step s; within a 64-K stage the lanes of half h = l / 32
@@ -76,15 +77,12 @@ __device__ __forceinline__ bf16x8 decode8(uint32_t lo, uint32_t hi) {
     p[2] = pack_bf16x2(sbyte<0>(hi), sbyte<1>(hi));
     p[3] = pack_bf16x2(sbyte<2>(hi), sbyte<3>(hi));
   } else {
-    typedef float f2 __attribute__((ext_vector_type(2)));
-    f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
-    f2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
-    f2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
-    f2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-    p[0] = pack_bf16x2(a[0], a[1]);
-    p[1] = pack_bf16x2(b[0], b[1]);
-    p[2] = pack_bf16x2(c[0], c[1]);
-    p[3] = pack_bf16x2(d[0], d[1]);
+    // E4M3 -> bf16 is exact; the scaled pair conversion with scale 1 turns
+    // two codes into two bf16 values in one instruction
+    p[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+    p[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+    p[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+    p[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
   }
   return __builtin_bit_cast(bf16x8, p);
 }

@@ -30,8 +30,9 @@
 // two stages ahead. Each 128-K group's products accumulate from zero and are
 // folded into the float32 result with the group's scale (int8: the column's;
 // E4M3: block scale times the pass row's sx); v_mfma_f32_32x32x16_bf16 on
-// codes decoded to bf16 exactly (int8 by byte converts, E4M3 by
-// v_cvt_pk_f32_fp8: both fit bf16's significand).
+// codes decoded to bf16 exactly (int8 by byte converts, E4M3 two codes an
+// instruction by v_cvt_scalef32_pk_bf16_fp8 with scale 1: both fit bf16's
+// significand).
 //
 // Stage layouts as in the larger kernels: A piece p (8 bf16) of row r (128
 // bytes) at p ^ ((r >> 1) & 7), B piece p (16 codes) of row r (64 bytes) at
@@ -122,15 +123,12 @@ __device__ __forceinline__ bf16x8 s_decode(uint32_t lo, uint32_t hi) {
     p[2] = pack_bf16x2(sbyte<0>(hi), sbyte<1>(hi));
     p[3] = pack_bf16x2(sbyte<2>(hi), sbyte<3>(hi));
   } else {
-    typedef float f2 __attribute__((ext_vector_type(2)));
-    const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
-    const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
-    const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
-    const f2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-    p[0] = pack_bf16x2(a[0], a[1]);
-    p[1] = pack_bf16x2(b[0], b[1]);
-    p[2] = pack_bf16x2(c[0], c[1]);
-    p[3] = pack_bf16x2(d[0], d[1]);
+    // E4M3 -> bf16 is exact; the scaled pair conversion with scale 1 turns
+    // two codes into two bf16 values in one instruction
+    p[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+    p[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+    p[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+    p[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
   }
   return __builtin_bit_cast(bf16x8, p);
 }
