@@ -1,8 +1,9 @@
 """GPU parity on seeded random shapes: every entry of the hot path against the oracle.
 
 Each case draws T, K, E, topk and N from a fixed seed (small and large token
-counts, K up to 5120, up to 256 experts, topk up to 32, N from 64 to 2048)
-and runs, on the generator's inputs:
+counts, K up to 5120, up to 256 experts, topk up to 32, N from 64 to 2048);
+two more take 1024 experts with top-32 and top-k equal to the expert count.
+Each runs, on the generator's inputs:
   - routing + rotation: ids, expert_off, sorted_pairs and pair_pos equal to
     the oracle's, weights within 1e-4 relative + 1e-5, x_rot equal up to the
     proven float32 tie window;
@@ -51,7 +52,10 @@ def _draw_cases(n, seed):
     return out
 
 
-CASES = _draw_cases(32, 20261203)
+# plus the limits the entry points accept: the most experts (1024) with the
+# largest top-k (32), and top-k equal to the expert count (every token in
+# every expert)
+CASES = _draw_cases(32, 20261203) + [(300, 256, 1024, 32, 128, 7100), (65, 384, 32, 32, 192, 7101)]
 
 
 def _sample_rows(off, rng, n=24):
