@@ -171,3 +171,35 @@ def test_routing_without_workspace():
         i8h.moe_route_permute_noalloc(lg, L.topk, out=r)
     _check_replays([lg], [[lgs[0]], [lgs[1]]], fn,
                    lambda: [r[k] for k in ("topk_ids", "topk_w", "expert_off", "sorted_pairs", "pair_pos")])
+
+
+def test_decode_two_launch():
+    """Decode as routing, then the gate_up call that rotates inside its GEMV (a batch of 4 tokens)."""
+    L, lgs, xs = _layer("decode", T=4)
+    codes, sbits = synth.synthetic_i8h(L)
+    codes, scales = torch.from_numpy(codes).cuda(), bf16_cuda(sbits)
+    lg, x = lgs[0].clone(), xs[0].clone()
+    r = i8h.moe_route_permute(lg, L.topk)
+    gu = torch.empty((L.P, L.N), device="cuda")
+    act = torch.empty((L.P, L.I), device="cuda")
+
+    def fn():
+        i8h.moe_route_permute(lg, L.topk, out=r)
+        i8h.moe_gateup_i8h_grouped_fused(x, codes, scales, L.topk, r["expert_off"], r["sorted_pairs"],
+                                         gate_up=gu, act=act)
+    _check_replays([lg, x], [[lgs[0], xs[0]], [lgs[1], xs[1]]], fn, lambda: [gu, act, r["sorted_pairs"]])
+
+
+def test_drafter_linear():
+    """The drafter's int8 linear (16 positions, K = 2048, N = 4096)."""
+    T, K, N = 16, 2048, 4096
+    codes, sbits = synth.synthetic_i8f16(N, K, seed=31)
+    codes = torch.from_numpy(codes).cuda()
+    scales = torch.from_numpy(sbits.view(np.float16)).cuda()
+    xb = [bf16_cuda(synth.drafter_activations_bf16(T, K, seed)) for seed in (32, 33)]
+    x = xb[0].clone()
+    y = torch.empty((T, N), device="cuda")
+
+    def fn():
+        i8h.linear_i8f16(x, codes, scales, out=y)
+    _check_replays([x], [[xb[0]], [xb[1]]], fn, lambda: [y])
