@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--read-probe", action="store_true",
                     help="only run the HBM read-bandwidth probe (streaming and one-shot decode-sized reads) "
                          "and print its JSON line")
+    ap.add_argument("--overlap-probe", action="store_true",
+                    help="only run the MFMA / VALU overlap probe (time per MFMA with N FMAs beside it, one and "
+                         "two waves a SIMD) and print its JSON line")
     ap.add_argument("--two-launch", action="store_true",
                     help="decode: time moe_route_permute + moe_gateup_i8h_grouped_fused instead of the "
                          "one-launch moe_route_gateup_i8h_decode")
@@ -165,6 +168,9 @@ def main():
         return
     if args.read_probe:
         print(json.dumps({"read_probe": read_probe(dev)}))
+        return
+    if args.overlap_probe:
+        print(json.dumps({"overlap_probe": overlap_probe(dev)}))
         return
     i8h.lib()
 
@@ -483,6 +489,46 @@ def read_probe(dev):
     del bufs, sink
     torch.cuda.empty_cache()
     return out
+
+
+def overlap_probe(dev):
+    """How much VALU work hides under the MFMAs (libi8h_probe.so): a workgroup
+    per CU, one or two waves a SIMD, four independent 32x32x16 bf16 MFMA
+    chains a wave with N independent float FMAs after each MFMA. Per N: the
+    time per MFMA and wave (best of 3 launches after one untimed), also in
+    clocks at the nominal 2.4 GHz."""
+    import ctypes
+    import torch
+    here = os.path.dirname(os.path.abspath(__file__))
+    P = ctypes.CDLL(os.path.join(here, "int8_hadamard_domain_amd", "lib", "libi8h_probe.so"))
+    P.i8h_overlap_probe.restype = ctypes.c_int
+    P.i8h_overlap_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 20000
+    out_buf = torch.empty(cus * 512, dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream(dev)
+    res = {"cus": cus, "iters": iters, "mfma": "v_mfma_f32_32x32x16_bf16, 4 chains a wave", "valu": "v_fma_f32"}
+    for threads in (256, 512):
+        rows = {}
+        for n in (0, 2, 4, 6, 8, 12, 16):
+            best = None
+            for rep in range(4):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                rc = P.i8h_overlap_probe(n, threads, cus, iters, ctypes.c_void_p(out_buf.data_ptr()),
+                                         ctypes.c_void_p(st.cuda_stream))
+                e1.record(st)
+                if rc != 0:
+                    raise RuntimeError(f"i8h_overlap_probe failed ({rc})")
+                torch.cuda.synchronize(dev)
+                if rep > 0:
+                    t = e0.elapsed_time(e1) * 1e-3 / (4 * iters)
+                    best = t if best is None else min(best, t)
+            rows[str(n)] = {"ns_per_mfma": round(best * 1e9, 2), "clk_2p4ghz": round(best * 2.4e9, 1)}
+        res[f"waves_per_simd_{threads // 256}"] = rows
+    del out_buf
+    return res
 
 
 # device-code sources of each timed kernel: a traffic figure holds only for the sources it was

@@ -1,9 +1,10 @@
 /*
  * i8h_probe — measurement probes beside the library (libi8h_probe.so; not
  * part of the product path): an HBM read-bandwidth probe, the ceiling the
- * HBM-bound kernels are measured against on the same GPU, and an FP8
+ * HBM-bound kernels are measured against on the same GPU, an FP8
  * matrix-core precision probe, which runs gfx950's native E4M3 MFMA forms on
- * caller data so that their sums can be compared with exact ones.
+ * caller data so that their sums can be compared with exact ones, and a
+ * matrix-core / vector-ALU overlap probe.
  */
 #ifndef I8H_PROBE_H
 #define I8H_PROBE_H
@@ -41,6 +42,17 @@ int i8h_read_probe(const void* buf, size_t bytes, int blocks, uint32_t key, uint
  * launched. Returns 0, or -3 when the HIP runtime refuses the launch.
  * Enqueued on `stream` (hipStream_t as void*). */
 int i8h_fp8_mfma_probe(int form, const void* a, const void* b, float* c, int tiles, int steps, void* stream);
+
+/* MFMA / VALU overlap: `blocks` workgroups of `threads` (256 or 512: one or
+ * two waves a SIMD with one workgroup a CU) threads, each wave running
+ * `iters` iterations of four independent v_mfma_f32_32x32x16_bf16
+ * accumulation chains with `nvalu` (0, 2, 4, 6, 8, 12 or 16) independent
+ * float FMAs after each MFMA, in that order. out: device float32 array of
+ * blocks * threads values (one sum per thread, caller-owned, 4-B aligned).
+ * The caller times the launch; launch time / (4 iters) is the time per MFMA
+ * and wave. Invalid arguments: -1, nothing launched. Returns 0, or -3 when
+ * the HIP runtime refuses the launch. Enqueued on `stream`. */
+int i8h_overlap_probe(int nvalu, int threads, int blocks, int iters, float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -19,9 +19,10 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "obj")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libi8h.so")
-# the measurement probes (HBM read bandwidth, FP8 matrix-core precision): their own library
+# the measurement probes (HBM read bandwidth, FP8 matrix-core precision, MFMA/VALU overlap):
+# their own library
 PROBE_LIB = os.path.join(LIBDIR, "libi8h_probe.so")
-PROBE_SOURCES = ["probe.hip", "probe_fp8_mfma.hip"]
+PROBE_SOURCES = ["probe.hip", "probe_fp8_mfma.hip", "probe_overlap.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

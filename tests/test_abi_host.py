@@ -327,7 +327,7 @@ def test_probe_library_exports_and_validation():
     P = ctypes.CDLL(PROBE_LIB)
     src = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b([a-z][a-z0-9_]*)\s*\(", src)) - {"defined"})
-    assert names == ["i8h_fp8_mfma_probe", "i8h_read_probe"], names
+    assert names == ["i8h_fp8_mfma_probe", "i8h_overlap_probe", "i8h_read_probe"], names
     for n in names:
         assert hasattr(P, n), n
     f = P.i8h_fp8_mfma_probe
@@ -346,3 +346,11 @@ def test_probe_library_exports_and_validation():
     assert r(A, 24, 1, 0, A, None) == -1
     assert r(A, 32, 0, 0, A, None) == -1
     assert r(ODD, 32, 1, 0, A, None) == -1
+    o = P.i8h_overlap_probe
+    o.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert o(5, 256, 1, 1, A, None) == -1                            # no such VALU count
+    assert o(4, 128, 1, 1, A, None) == -1                            # 256 or 512 threads
+    assert o(4, 256, 0, 1, A, None) == -1
+    assert o(4, 256, 1, 0, A, None) == -1
+    assert o(4, 256, 1, 1, None, None) == -1
+    assert o(4, 256, 1, 1, ODD, None) == -1
